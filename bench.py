@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path on resident synthetic inputs:
+  1. causal prefill attn_fwd on the GPT-2-small-shaped workload
+     (B=8, H=12, T=S=1024, d=64, bf16; override with --prefill), then
+  2. paged decode attn_decode_paged on 64 sequences, 12 query / 2 KV heads,
+     d=128, 16-token pages, lengths U[512, 8192] (split kernel + combine).
+
+Reported (one JSON line on stdout):
+  value          causal-prefill TFLOP/s = algorithmic FLOPs / mean kernel time
+                 (HIP events on the launch stream), FLOPs = 4*d per visible
+                 (query, key) pair;
+  decode         paged-decode GB/s = algorithmic bytes / mean time of the split
+                 + combine kernels, bytes = K+V of every cached token once plus
+                 q, o, lse, seq_lens and the used block-table entries;
+  roofline       the kernel that takes the most time per step against its
+                 published peak (bf16 dense MFMA 2516.6 TFLOP/s, HBM 8 TB/s);
+                 `traffic` comes from profiles/counters.json when the measured
+                 kernel sources still match the recorded hash, else null;
+  cpu_baseline   the float64 oracle timed on the host on a bounded sample of
+                 the same workloads.
+Between steps a 512 MiB buffer is overwritten so both kernels start with
+cold L2 / Infinity Cache; that fill is outside the kernel events but inside
+ms_per_step.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = {
+    "prefill": ["tiled_exact_attention_flashattention_amd/csrc/prefill_bf16.hip",
+                "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp"],
+    "decode": ["tiled_exact_attention_flashattention_amd/csrc/decode_paged.hip",
+               "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp"],
+}
+
+
+def sources_sha(kind):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_work(B, Hq, Hkv, T, S, d, causal, elem):
+    if causal:
+        pairs = sum(min(S, i + (S - T) + 1) for i in range(T))
+    else:
+        pairs = T * S
+    flops = 4 * d * pairs * B * Hq
+    nbytes = (2 * B * Hq * T * d + 2 * B * Hkv * S * d) * elem + B * Hq * T * 4
+    return flops, nbytes
+
+
+def decode_work(inp):
+    tokens = int(inp.seq_lens.astype("int64").sum())
+    pages = int(((inp.seq_lens.astype("int64") + inp.page - 1) // inp.page).sum())
+    kv = tokens * inp.Hkv * inp.d * 2 * 2
+    qo = 2 * inp.N * inp.Hq * inp.d * 2
+    nbytes = kv + qo + inp.N * inp.Hq * 4 + inp.N * 4 + pages * 4
+    flops = 4 * inp.d * tokens * inp.Hq
+    return flops, nbytes, tokens
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def cpu_baseline(pinp, dinp, budget_s):
+    """Time the oracle on a bounded sample of both workloads (host cores)."""
+    import numpy as np
+
+    import oracle
+    q, k, v = (t.double().numpy() for t in (pinp.q, pinp.k, pinp.v))
+    g = pinp.Hq // pinp.Hkv
+    heads = [(b, h) for b in range(pinp.B) for h in range(pinp.Hq)]
+    done, flops, t0 = 0, 0, time.perf_counter()
+    for (b, h) in heads:
+        oracle.attention_head(q[b, h], k[b, h // g], v[b, h // g], pinp.scale, pinp.causal)
+        done += 1
+        flops += prefill_work(1, 1, 1, pinp.T, pinp.S, pinp.d, pinp.causal, 2)[0]
+        if time.perf_counter() - t0 > budget_s * 0.7:
+            break
+    tp = time.perf_counter() - t0
+    qd, kd, vd = dinp.f64()
+    nseq, dbytes, t1 = 0, 0, time.perf_counter()
+    for n in range(dinp.N):
+        oracle.decode_paged(qd, kd, vd, dinp.block_table, dinp.seq_lens, dinp.scale, seqs=[n])
+        L = int(dinp.seq_lens[n])
+        dbytes += L * dinp.Hkv * dinp.d * 4 + 2 * dinp.Hq * dinp.d * 2
+        nseq += 1
+        if time.perf_counter() - t1 > budget_s * 0.3:
+            break
+    td = time.perf_counter() - t1
+    return {
+        "value": flops / tp / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+        "sample": f"{done} of {len(heads)} (batch, head) pairs of {pinp.name} "
+                  f"({tp:.1f} s); decode: {nseq} of {dinp.N} sequences of {dinp.name} ({td:.1f} s)",
+        "decode_value": dbytes / td / 1e9, "decode_unit": "GB/s",
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def counters_for(kind):
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("sources_sha") != sources_sha(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill", default="prefill_2",
+                    choices=["prefill_2", "prefill_3", "prefill_4"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle work")
+    ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 256 MiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "the kernels run on one device's share and nothing here is sharded.", flush=True)
+        sys.exit(1)
+
+    import torch
+
+    import tiled_exact_attention_flashattention_amd as tea
+    import workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe:
+        src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 256 << 20, "launches": 5}))
+        return
+
+    pinp = getattr(workloads, args.prefill)()
+    dinp = workloads.decode_5()
+    q, k, v = (t.to(dev) for t in (pinp.q, pinp.k, pinp.v))
+    o = torch.empty_like(q)
+    lse = torch.empty((pinp.B, pinp.Hq, pinp.T), dtype=torch.float32, device=dev)
+    dq, dk, dv = dinp.q.to(dev), dinp.k_pool.to(dev), dinp.v_pool.to(dev)
+    bt = torch.from_numpy(dinp.block_table).to(dev)
+    sl = torch.from_numpy(dinp.seq_lens).to(dev)
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dinp.N, dinp.Hq), dtype=torch.float32, device=dev)
+    ws = tea.decode_workspace(dinp.N, dinp.Hq, dinp.d, dinp.max_blocks, dev)
+    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+    events = []
+
+    def step(record):
+        if flush is not None:
+            flush.fill_(1)
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+        if record:
+            e[0].record(stream)
+        tea.attn_fwd(q, k, v, o, lse, pinp.scale, pinp.causal, stream=stream)
+        if record:
+            e[1].record(stream)
+            e[2].record(stream)
+        tea.attn_decode_paged(dq, dk, dv, bt, sl, do, dlse, dinp.scale, ws, stream=stream)
+        if record:
+            e[3].record(stream)
+            events.append(e)
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
+    decode_ms = sum(e[2].elapsed_time(e[3]) for e in events) / len(events)
+
+    elem = 2 if pinp.dtype == "bf16" else 4
+    pflops, pbytes = prefill_work(pinp.B, pinp.Hq, pinp.Hkv, pinp.T, pinp.S, pinp.d, pinp.causal, elem)
+    dflops, dbytes, tokens = decode_work(dinp)
+    p_tflops = pflops / (prefill_ms * 1e-3) / 1e12
+    d_gbs = dbytes / (decode_ms * 1e-3) / 1e9
+    peak_p = PEAK_BF16_TFLOPS if pinp.dtype == "bf16" else PEAK_F32_TFLOPS
+
+    kernels = {
+        "prefill": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": p_tflops,
+                    "peak": peak_p, "unit": "TFLOP/s", "frac": p_tflops / peak_p,
+                    "traffic": counters_for("prefill"), "algorithmic_bytes": pbytes,
+                    "algorithmic_flops": pflops, "ms": prefill_ms},
+        "decode": {"kernel": "decode_split_kernel+decode_combine_kernel", "bound": "hbm",
+                   "achieved": d_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": d_gbs / PEAK_HBM_GBS, "traffic": counters_for("decode"),
+                   "algorithmic_bytes": dbytes, "algorithmic_flops": dflops, "ms": decode_ms},
+    }
+    dominant = "prefill" if prefill_ms >= decode_ms else "decode"
+
+    out = {
+        "metric": "causal prefill attention TFLOP/s + paged decode GB/s, % of MFMA/HBM peak",
+        "value": p_tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": pinp.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": f"{pinp.name} causal prefill (B={pinp.B}, Hq={pinp.Hq}, Hkv={pinp.Hkv}, "
+                        f"T=S={pinp.T}, d={pinp.d}, {pinp.dtype}) + {dinp.name} paged decode "
+                        f"(N={dinp.N}, Hq={dinp.Hq}, Hkv={dinp.Hkv}, d={dinp.d}, page {dinp.page}, "
+                        f"lengths U[512,8192], sum {tokens})",
+            "global_batch": pinp.B,
+            "seq_len": pinp.T,
+            "parallelism": "single GPU",
+            "cold_cache": flush is not None,
+        },
+        "decode": {"value": d_gbs, "unit": "GB/s", "frac_of_hbm_peak": d_gbs / PEAK_HBM_GBS,
+                   "ms": decode_ms, "tokens": tokens},
+        "prefill_frac_of_mfma_peak": p_tflops / peak_p,
+        "roofline": dict(kernels[dominant]),
+        "roofline_per_kernel": kernels,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(pinp, dinp, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) tiled exact attention library.
+ *
+ * Two operations, each computing exactly softmax(scale * Q K^T) V without the
+ * score matrix ever reaching device memory:
+ *
+ *   attn_fwd           prefill: every query row of a sequence against its keys,
+ *                      optionally causal, with grouped-query heads, writing O
+ *                      and the per-row log-sum-exp.
+ *   attn_decode_paged  decode: one query token per sequence against a key/value
+ *                      cache stored in fixed-size pages reached through a
+ *                      block table.
+ *
+ * Definitions (page titles and sections of the sources):
+ *   - "Advanced Attention Mechanisms - II" (A. Das), section Tiling, steps 1-3:
+ *     Q, K, V are cut into tiles; per Q/K tile pair the scaled dot product
+ *     gives a tile of scores that is softmax-weighted against the V tile, and
+ *     the per-tile results accumulate into the full attention result.
+ *   - same page, sections "Softmax stabiliser" and "Incremental / online
+ *     softmax": the max-subtracted softmax, computed block by block with the
+ *     normaliser incomplete until the last block.
+ *   - same page, section "Flash Attention": the attention matrix is neither
+ *     read from nor written to device memory; only row statistics are kept.
+ *   - "Fast attention kernels and operator fusion accelerate AI models",
+ *     section on FlashAttention-style and paged attention: blocks of scores,
+ *     softmax statistics updated and outputs accumulated on chip; the paged KV
+ *     cache with its block table of logical-to-physical blocks; 16-token
+ *     blocks in the serving example.
+ *   - "Accelerating Mamba-2 with high-performance forward-pass kernels in
+ *     NVIDIA CUDA Tile": causal masking removes terms with i < j; exp2 with
+ *     log2(e) folded into the scale.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees, or synchronises, and keeps no state between calls.
+ *   - Tensors are dense row-major (C order) with the shapes given below.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Work is enqueued asynchronously on it; results are valid once the stream
+ *     has reached the point after the call.
+ *   - Every argument check happens on the host before any HIP call.  A call
+ *     that returns anything other than ATTN_OK has enqueued nothing.
+ *   - There is no fallback path: an unsupported input returns
+ *     ATTN_EUNSUPPORTED rather than being computed some other way.
+ *   - attn_last_error() returns a human-readable detail for the calling
+ *     thread's most recent non-OK return.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_EINVAL = 1,        /* bad pointer, size, alignment or combination      */
+  ATTN_EUNSUPPORTED = 2,  /* well-formed but outside what the kernels handle  */
+  ATTN_EHIP = 3           /* the HIP runtime reported an error at launch      */
+} attn_status;
+
+typedef enum {
+  ATTN_F32 = 0,           /* float32 q/k/v/o                                   */
+  ATTN_BF16 = 1           /* bfloat16 q/k/v/o, float32 accumulation            */
+} attn_dtype;
+
+/*
+ * attn_fwd -- prefill attention with log-sum-exp.
+ *
+ *   q   [B, Hq,  T, d]  dtype        queries
+ *   k   [B, Hkv, S, d]  dtype        keys
+ *   v   [B, Hkv, S, d]  dtype        values
+ *   o   [B, Hq,  T, d]  dtype        output (written)
+ *   lse [B, Hq,  T]     float32      natural-log log-sum-exp of the scaled
+ *                                    logits of each row (written); may be NULL
+ *
+ * O[b,h,i,:] = sum_j P[i,j] V[b,hk,j,:] with P = softmax_j(scale * q_i . k_j)
+ * over the visible keys j, where hk = h / (Hq / Hkv) (consecutive query heads
+ * share a KV head; Hq == Hkv is ordinary multi-head, Hkv == 1 multi-query).
+ * causal != 0 hides key j from query i when j > i + (S - T) (bottom-right
+ * alignment; the usual j > i when T == S).  bf16 outputs are rounded to
+ * nearest even from float32.
+ *
+ * Requirements: B, Hq, Hkv, T, S >= 1; Hq % Hkv == 0; causal implies T <= S;
+ * scale finite and > 0; q, k, v, o 16-byte aligned, lse 4-byte aligned;
+ * o and lse must not overlap q, k, v or each other.  d must be 64 or 128 (else
+ * ATTN_EUNSUPPORTED); dtype ATTN_F32 or ATTN_BF16.
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
+             int dtype, void* stream);
+
+/*
+ * attn_decode_paged -- one query token per sequence against a paged KV cache.
+ *
+ *   q           [N, Hq, d]                       bf16   queries (one per sequence)
+ *   k_pool      [num_pages, Hkv, page, d]        bf16   key pages
+ *   v_pool      [num_pages, Hkv, page, d]        bf16   value pages
+ *   block_table [N, max_blocks]                  int32  physical page of each
+ *                                                       logical block
+ *   seq_lens    [N]                              int32  cached tokens per sequence
+ *   o           [N, Hq, d]                       bf16   output (written)
+ *   lse         [N, Hq]                          float32 log-sum-exp (written);
+ *                                                       may be NULL
+ *   workspace   >= attn_decode_workspace_size(N, Hq, d, max_blocks, page) bytes,
+ *               16-byte aligned, device memory; scratch for the split partials,
+ *               contents on entry are ignored.
+ *
+ * Token t of sequence n sits in page block_table[n, t / page] at slot
+ * t % page.  The query attends every cached token t < seq_lens[n] (no mask
+ * beyond the length).  The key range is cut into splits that are processed
+ * independently and merged by their log-sum-exp; the split size only changes
+ * rounding.
+ *
+ * Requirements checked on the host: N, Hq, Hkv, num_pages, max_blocks >= 1;
+ * Hq % Hkv == 0; scale finite and > 0; pointers aligned as for attn_fwd
+ * (block_table, seq_lens 4-byte).  page must be 16, d 64 or 128, dtype
+ * ATTN_BF16 and Hq / Hkv <= 16, else ATTN_EUNSUPPORTED.
+ *
+ * Device contents are a caller contract: 0 <= seq_lens[n] <= max_blocks*page
+ * and block_table[n, b] in [0, num_pages) for b < ceil(seq_lens[n] / page);
+ * entries past the end are never read.  The kernels never dereference a page
+ * outside [0, num_pages) (such a block is skipped, and that sequence's output
+ * is then unspecified), clamp lengths above max_blocks*page, and give a
+ * sequence of length 0 the output 0 and log-sum-exp -inf.  Slots of a page at
+ * or past the sequence length are never used, whatever they hold.
+ */
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens,
+                      void* o, float* lse,
+                      int N, int Hq, int Hkv, int d, int page, int num_pages,
+                      int max_blocks, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid). */
+size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page);
+
+/* Static English name of a status code. */
+const char* attn_status_string(int status);
+
+/* Detail of the calling thread's last non-OK return ("" if none yet). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,153 @@
+"""CPU tests of the C ABI boundary (no GPU, no kernel launches).
+
+The library must load, export every function that include/attn.h declares,
+and reject bad arguments on the host with the documented status codes before
+any HIP call.  Every call below violates at least one documented requirement,
+so nothing is ever launched and the fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import tiled_exact_attention_flashattention_amd as tea
+from tiled_exact_attention_flashattention_amd import (ATTN_BF16, ATTN_EINVAL, ATTN_EUNSUPPORTED,
+                                                      ATTN_F32)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert _declared_functions() == ["attn_decode_paged", "attn_decode_workspace_size", "attn_fwd",
+                                     "attn_last_error", "attn_status_string"]
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = tea.lib()
+    raw = ctypes.CDLL(tea.library_path())
+    for name in _declared_functions():
+        assert hasattr(raw, name), name
+        assert getattr(L, name) is not None
+
+
+def test_status_strings():
+    assert tea.attn_status_string(0) == "ATTN_OK"
+    assert tea.attn_status_string(ATTN_EINVAL).startswith("ATTN_EINVAL")
+    assert tea.attn_status_string(ATTN_EUNSUPPORTED).startswith("ATTN_EUNSUPPORTED")
+    assert tea.attn_status_string(3).startswith("ATTN_EHIP")
+    assert "unknown" in tea.attn_status_string(99)
+
+
+def test_workspace_size_formula():
+    # 64 sequences, 12 heads, d=128, 512 blocks: 32 splits of 16 pages
+    o_bytes = 64 * 12 * 32 * 128 * 4
+    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == o_bytes + 64 * 12 * 32 * 4
+    assert tea.attn_decode_workspace_size(1, 1, 64, 1, 16) == 256 + 4
+    assert tea.attn_decode_workspace_size(0, 12, 128, 512, 16) == 0
+    assert tea.attn_decode_workspace_size(4, 12, 128, 512, 8) == 0
+
+
+# --- attn_fwd argument checks --------------------------------------------------
+
+P = 1 << 20     # fake, 16-byte aligned, never dereferenced
+FWD_OK = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, B=1, Hq=4, Hkv=2, T=64, S=64, d=64,
+              scale=0.125, causal=1, dtype=ATTN_BF16, stream=None)
+
+
+def _fwd(**kw):
+    a = dict(FWD_OK)
+    a.update(kw)
+    return tea.lib().attn_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                              a["T"], a["S"], a["d"], a["scale"], a["causal"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), ATTN_EINVAL), (dict(k=None), ATTN_EINVAL), (dict(v=None), ATTN_EINVAL),
+    (dict(o=None), ATTN_EINVAL),
+    (dict(B=0), ATTN_EINVAL), (dict(Hq=0), ATTN_EINVAL), (dict(Hkv=0), ATTN_EINVAL),
+    (dict(T=0), ATTN_EINVAL), (dict(S=0), ATTN_EINVAL), (dict(d=0), ATTN_EINVAL),
+    (dict(T=-3), ATTN_EINVAL),
+    (dict(Hq=5, Hkv=2), ATTN_EINVAL),
+    (dict(T=65, S=64, causal=1), ATTN_EINVAL),
+    (dict(scale=0.0), ATTN_EINVAL), (dict(scale=-0.1), ATTN_EINVAL),
+    (dict(scale=float("nan")), ATTN_EINVAL), (dict(scale=float("inf")), ATTN_EINVAL),
+    (dict(d=96), ATTN_EUNSUPPORTED), (dict(d=256), ATTN_EUNSUPPORTED), (dict(d=32), ATTN_EUNSUPPORTED),
+    (dict(dtype=7), ATTN_EUNSUPPORTED),
+    (dict(q=P + 8), ATTN_EINVAL), (dict(k=2 * P + 4), ATTN_EINVAL), (dict(o=4 * P + 2), ATTN_EINVAL),
+    (dict(lse=5 * P + 2), ATTN_EINVAL),
+    (dict(o=P), ATTN_EINVAL),                    # output aliases q
+    (dict(lse=4 * P + 64), ATTN_EINVAL),         # lse inside o
+    (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, T=1 << 12), ATTN_EINVAL),   # too large
+])
+def test_fwd_rejects_bad_arguments(bad, code):
+    assert _fwd(**bad) == code
+    assert tea.attn_last_error().startswith("attn_fwd")
+
+
+def test_fwd_f32_shares_the_checks():
+    assert _fwd(dtype=ATTN_F32, d=80) == ATTN_EUNSUPPORTED
+    assert _fwd(dtype=ATTN_F32, T=100, S=50) == ATTN_EINVAL
+
+
+# --- attn_decode_paged argument checks ------------------------------------------
+
+WS = tea.attn_decode_workspace_size(8, 12, 128, 64, 16)
+DEC_OK = dict(q=P, k=2 * P, v=3 * P, bt=4 * P, lens=5 * P, o=6 * P, lse=7 * P, N=8, Hq=12, Hkv=2,
+              d=128, page=16, num_pages=100, max_blocks=64, scale=0.088, dtype=ATTN_BF16,
+              ws=8 * P, ws_bytes=WS, stream=None)
+
+
+def _dec(**kw):
+    a = dict(DEC_OK)
+    a.update(kw)
+    return tea.lib().attn_decode_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"], a["lse"],
+                                       a["N"], a["Hq"], a["Hkv"], a["d"], a["page"], a["num_pages"],
+                                       a["max_blocks"], a["scale"], a["dtype"], a["ws"],
+                                       a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), ATTN_EINVAL), (dict(k=None), ATTN_EINVAL), (dict(v=None), ATTN_EINVAL),
+    (dict(bt=None), ATTN_EINVAL), (dict(lens=None), ATTN_EINVAL), (dict(o=None), ATTN_EINVAL),
+    (dict(N=0), ATTN_EINVAL), (dict(Hq=0), ATTN_EINVAL), (dict(Hkv=0), ATTN_EINVAL),
+    (dict(num_pages=0), ATTN_EINVAL), (dict(max_blocks=0), ATTN_EINVAL),
+    (dict(Hq=12, Hkv=5), ATTN_EINVAL),
+    (dict(scale=0.0), ATTN_EINVAL), (dict(scale=float("nan")), ATTN_EINVAL),
+    (dict(dtype=ATTN_F32), ATTN_EUNSUPPORTED), (dict(page=8), ATTN_EUNSUPPORTED),
+    (dict(page=32), ATTN_EUNSUPPORTED), (dict(d=96), ATTN_EUNSUPPORTED),
+    (dict(Hq=34, Hkv=2), ATTN_EUNSUPPORTED),
+    (dict(q=P + 4), ATTN_EINVAL), (dict(bt=4 * P + 2), ATTN_EINVAL),
+    (dict(ws=None), ATTN_EINVAL), (dict(ws_bytes=WS - 1), ATTN_EINVAL), (dict(ws=8 * P + 8), ATTN_EINVAL),
+])
+def test_decode_rejects_bad_arguments(bad, code):
+    assert _dec(**bad) == code
+    assert tea.attn_last_error().startswith("attn_decode_paged")
+
+
+def test_python_binding_rejects_host_tensors():
+    import torch
+    q = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tea.attn_fwd(q, q, q, torch.empty_like(q), None, 0.125, False)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import tiled_exact_attention_flashattention_amd._binding as b
+    monkeypatch.setattr(b, "_LIB", None)
+    monkeypatch.setattr(b, "LIB_PATH", str(tmp_path / "libattn.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        b.lib()
+
+
+def test_one_hip_runtime_per_process():
+    """libattn.so must bind to torch's HIP runtime, never map a second one."""
+    import tiled_exact_attention_flashattention_amd._binding as b
+    tea.lib()
+    assert len(b.hip_runtimes_loaded()) == 1, b.hip_runtimes_loaded()

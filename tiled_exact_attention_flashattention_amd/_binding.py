@@ -1,0 +1,218 @@
+"""ctypes binding of libattn.so: argument marshalling only.
+
+Each function mirrors one entry point of ``include/attn.h`` under the same
+name.  Tensors are PyTorch tensors on a ROCm device; this module only reads
+their shapes, dtypes, devices and data pointers, picks the caller's current
+stream, and turns a non-OK status into :class:`AttnError`.  All computation
+happens in the HIP kernels.  If the library is not built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_EHIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+PAGE = 16
+
+_LIB = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{attn_status_string(status)} ({detail})")
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def hip_runtimes_loaded() -> list:
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) >= 6 and "libamdhip64" in parts[-1]:
+                    paths.add(os.path.realpath(parts[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it was never built).
+
+    torch is imported first so that its HIP runtime is the one in the process:
+    libattn.so asks for ``libamdhip64.so.7``, which the loader then satisfies
+    with torch's copy (same SONAME).  Loaded the other way round, torch would
+    map a second HIP runtime next to the system one, and device pointers and
+    streams from one runtime are meaningless to the other.
+    """
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m tiled_exact_attention_flashattention_amd.build` (there is no fallback)")
+    import torch  # noqa: F401  (must precede the CDLL below)
+    L = ctypes.CDLL(LIB_PATH)
+    runtimes = hip_runtimes_loaded()
+    if len(runtimes) > 1:
+        raise RuntimeError(f"more than one HIP runtime is mapped into this process: {runtimes}")
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32, vp]
+    L.attn_fwd.restype = i32
+    L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
+                                    f32, i32, vp, sz, vp]
+    L.attn_decode_paged.restype = i32
+    L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_decode_workspace_size.restype = sz
+    L.attn_status_string.argtypes = [i32]
+    L.attn_status_string.restype = ctypes.c_char_p
+    L.attn_last_error.argtypes = []
+    L.attn_last_error.restype = ctypes.c_char_p
+    _LIB = L
+    return L
+
+
+def attn_status_string(status: int) -> str:
+    return lib().attn_status_string(int(status)).decode()
+
+
+def attn_last_error() -> str:
+    return lib().attn_last_error().decode()
+
+
+def attn_decode_workspace_size(N: int, Hq: int, d: int, max_blocks: int, page: int = PAGE) -> int:
+    return int(lib().attn_decode_workspace_size(N, Hq, d, max_blocks, page))
+
+
+def _check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, attn_last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream_ptr(device, stream) -> int:
+    import torch
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _require_device_tensors(*ts) -> None:
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+
+
+def attn_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
+    """Enqueue attn_fwd on ``stream`` (default: the current stream of q's device).
+
+    q/o [B,Hq,T,d], k/v [B,Hkv,S,d] in one dtype (bf16 or f32); lse [B,Hq,T]
+    float32 or None.
+    """
+    import torch
+    _require_device_tensors(q, k, v, o, lse)
+    B, Hq, T, d = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, S, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise TypeError("q, k, v, o must share one dtype")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B, Hq, T)):
+        raise ValueError("lse must be float32 [B, Hq, T]")
+    st = lib().attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr() if lse is not None else None,
+                        B, Hq, Hkv, T, S, d, float(scale), int(bool(causal)), _dtype_code(q),
+                        _stream_ptr(q.device, stream))
+    _check(st)
+
+
+def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: float,
+                      workspace, page: int = PAGE, stream=None) -> None:
+    """Enqueue attn_decode_paged on ``stream``.
+
+    q/o [N,Hq,d] bf16; pools [num_pages,Hkv,page,d] bf16; block_table int32
+    [N,max_blocks]; seq_lens int32 [N]; lse float32 [N,Hq] or None;
+    workspace: a device tensor of at least attn_decode_workspace_size bytes.
+    """
+    import torch
+    _require_device_tensors(q, k_pool, v_pool, block_table, seq_lens, o, lse, workspace)
+    N, Hq, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    if k_pool.shape != (num_pages, Hkv, page, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [num_pages, Hkv, page, d]")
+    if o.shape != q.shape or block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("shape mismatch among q, o, block_table")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (N,):
+        raise TypeError("block_table and seq_lens must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
+        raise ValueError("lse must be float32 [N, Hq]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                 block_table.data_ptr(), seq_lens.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr() if lse is not None else None,
+                                 N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
+                                 float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes,
+                                 _stream_ptr(q.device, stream))
+    _check(st)
+
+
+# ---- conveniences that allocate outputs with torch ---------------------------
+
+def fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, with_lse: bool = True):
+    """Allocate O (and LSE) and run attn_fwd.  Returns (o, lse)."""
+    import torch
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
+    attn_fwd(q, k, v, o, lse, scale, causal)
+    return o, lse
+
+
+def decode_workspace(N: int, Hq: int, d: int, max_blocks: int, device) -> "object":
+    import torch
+    nbytes = attn_decode_workspace_size(N, Hq, d, max_blocks, PAGE)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def decode_paged(q, k_pool, v_pool, block_table, seq_lens, scale: Optional[float] = None,
+                 workspace=None, with_lse: bool = True):
+    """Allocate O (and LSE, and the workspace if not given) and run attn_decode_paged."""
+    import torch
+    N, Hq, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = decode_workspace(N, Hq, d, block_table.shape[1], q.device)
+    o = torch.empty_like(q)
+    lse = torch.empty((N, Hq), dtype=torch.float32, device=q.device) if with_lse else None
+    attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale, workspace)
+    return o, lse

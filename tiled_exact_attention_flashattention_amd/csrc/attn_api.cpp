@@ -1,0 +1,171 @@
+// attn_api.cpp -- the C ABI declared in include/attn.h.
+//
+// Every check runs on the host before any HIP call, so a rejected call has no
+// side effect on the device and can be exercised without a GPU.  An
+// unsupported input is reported, never computed some other way: forcing a
+// backend that cannot take the inputs is an error ("Fast attention kernels and
+// operator fusion accelerate AI models", section on FlashAttention-style
+// attention; the serving example checks backend compatibility up front).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Byte ranges [p, p+n) and [q, q+m) intersect.
+bool overlap(const void* p, size_t n, const void* q, size_t m) {
+  if (p == nullptr || q == nullptr || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+constexpr int kPage = 16;
+constexpr int kMinSplitPages = 16;    // workspace is sized for the smallest split
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+size_t workspace_bytes_for(int64_t N, int64_t Hq, int64_t d, int64_t max_blocks) {
+  const int64_t max_splits = (max_blocks + kMinSplitPages - 1) / kMinSplitPages;
+  const int64_t o_bytes = N * Hq * max_splits * d * 4;
+  const int64_t lse_bytes = N * Hq * max_splits * 4;
+  return (size_t)(((o_bytes + 255) / 256) * 256 + lse_bytes);
+}
+
+// Pages per split: the environment can pin it (even, >= 16); otherwise 32.
+int decode_split_pages() {
+  static int cached = [] {
+    const char* e = std::getenv("ATTN_DECODE_SPLIT_PAGES");
+    int v = e ? std::atoi(e) : 0;
+    if (v < kMinSplitPages || (v & 1)) v = 32;
+    return v;
+  }();
+  return cached;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_EINVAL: return "ATTN_EINVAL: invalid argument";
+    case ATTN_EUNSUPPORTED: return "ATTN_EUNSUPPORTED: input outside what the kernels support";
+    case ATTN_EHIP: return "ATTN_EHIP: HIP runtime error";
+    default: return "unknown attn status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error; }
+
+size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page) {
+  if (N < 1 || Hq < 1 || d < 1 || max_blocks < 1 || page != kPage) return 0;
+  return workspace_bytes_for(N, Hq, d, max_blocks);
+}
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int T, int S, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "attn_fwd: q, k, v and o must be non-NULL");
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1)
+    return fail(ATTN_EINVAL, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d T=%d S=%d d=%d)", B,
+                Hq, Hkv, T, S, d);
+  if (Hq % Hkv != 0) return fail(ATTN_EINVAL, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal && T > S)
+    return fail(ATTN_EINVAL, "attn_fwd: causal attention needs T <= S (T=%d S=%d)", T, S);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "attn_fwd: scale must be finite and > 0");
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16)
+    return fail(ATTN_EUNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "attn_fwd: head dim %d (need 64 or 128)", d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      (lse && !aligned(lse, 4)))
+    return fail(ATTN_EINVAL, "attn_fwd: q/k/v/o need 16-byte alignment, lse 4-byte");
+  const int64_t qn = (int64_t)B * Hq * T * d, kn = (int64_t)B * Hkv * S * d;
+  if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "attn_fwd: tensor too large");
+  const int64_t grid = ((int64_t)T + 127) / 128 * B * Hq;
+  if (grid > 0x7fffffff) return fail(ATTN_EINVAL, "attn_fwd: too many query tiles");
+  const size_t es = dtype == ATTN_BF16 ? 2 : 4;
+  const size_t qb = qn * es, kb = kn * es, lb = lse ? (size_t)B * Hq * T * 4 : 0;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) ||
+      overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
+      overlap(lse, lb, o, qb))
+    return fail(ATTN_EINVAL, "attn_fwd: o/lse overlap an input or each other");
+
+  const float scale_log2 = scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == ATTN_BF16
+                     ? attn::launch_prefill_bf16(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale_log2,
+                                                 causal != 0, st)
+                     : attn::launch_prefill_f32(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale_log2,
+                                                causal != 0, st);
+  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_fwd: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      int N, int Hq, int Hkv, int d, int page, int num_pages, int max_blocks,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
+    return fail(ATTN_EINVAL, "attn_decode_paged: tensor pointers must be non-NULL");
+  if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1 || max_blocks < 1 || page < 1)
+    return fail(ATTN_EINVAL, "attn_decode_paged: sizes must be >= 1");
+  if (Hq % Hkv != 0)
+    return fail(ATTN_EINVAL, "attn_decode_paged: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "attn_decode_paged: scale must be finite and > 0");
+  if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: only bf16 is supported");
+  if (page != kPage) return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: page size %d (need 16)", page);
+  if (d != 64 && d != 128)
+    return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: head dim %d (need 64 or 128)", d);
+  if (Hq / Hkv > 16)
+    return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: %d query heads per KV head (max 16)", Hq / Hkv);
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(ATTN_EINVAL, "attn_decode_paged: misaligned pointer");
+  if ((int64_t)max_blocks * kPage > 0x7fffffff || (int64_t)num_pages * Hkv * kPage * d > kMaxElems)
+    return fail(ATTN_EINVAL, "attn_decode_paged: cache too large");
+  if ((int64_t)N * Hq > 0x7fffffff / 1024 || N > 65535 || Hkv > 65535)
+    return fail(ATTN_EINVAL, "attn_decode_paged: N, Hkv or N*Hq too large");
+  const size_t need = workspace_bytes_for(N, Hq, d, max_blocks);
+  if (!workspace || workspace_bytes < need)
+    return fail(ATTN_EINVAL, "attn_decode_paged: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "attn_decode_paged: misaligned workspace");
+
+  const int max_splits = (max_blocks + kMinSplitPages - 1) / kMinSplitPages;
+  float* o_part = static_cast<float*>(workspace);
+  const size_t o_bytes = (size_t)N * Hq * max_splits * d * 4;
+  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o_bytes + 255) / 256) * 256);
+  const int split_pages = decode_split_pages();
+  hipError_t e = attn::launch_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, o_part,
+                                           lse_part, N, Hq, Hkv, d, num_pages, max_blocks,
+                                           split_pages, max_splits, scale * kLog2e,
+                                           static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_decode_paged: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+}  // extern "C"
