@@ -20,9 +20,9 @@ Reported (one JSON line on stdout):
                  kernel sources still match the recorded hash, else null;
   cpu_baseline   the float64 oracle timed on the host on a bounded sample of
                  the same workloads.
-Between steps a 512 MiB buffer is overwritten so both kernels start with
-cold L2 / Infinity Cache; that fill is outside the kernel events but inside
-ms_per_step.
+Between steps a 512 MiB buffer is read (summed) so both kernels start with
+cold L2 / Infinity Cache without dirty lines whose write-back would compete
+with them; that read is outside the kernel events but inside ms_per_step.
 """
 import argparse
 import hashlib
@@ -178,14 +178,14 @@ def main():
     do = torch.empty_like(dq)
     dlse = torch.empty((dinp.N, dinp.Hq), dtype=torch.float32, device=dev)
     ws = tea.decode_workspace(dinp.N, dinp.Hq, dinp.d, dinp.max_blocks, dev)
-    flush = None if args.no_flush else torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
 
     stream = torch.cuda.current_stream(dev)
     events = []
 
     def step(record):
         if flush is not None:
-            flush.fill_(1)
+            flush.sum()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
         if record:
             e[0].record(stream)

@@ -52,12 +52,13 @@ size_t workspace_bytes_for(int64_t N, int64_t Hq, int64_t d, int64_t max_blocks)
   return (size_t)(((o_bytes + 255) / 256) * 256 + lse_bytes);
 }
 
-// Pages per split: the environment can pin it (even, >= 16); otherwise 32.
+// Pages per split: the environment can pin it (even, 16..256, the page ids of
+// one split are staged in LDS); otherwise 32.
 int decode_split_pages() {
   static int cached = [] {
     const char* e = std::getenv("ATTN_DECODE_SPLIT_PAGES");
     int v = e ? std::atoi(e) : 0;
-    if (v < kMinSplitPages || (v & 1)) v = 32;
+    if (v < kMinSplitPages || v > 256 || (v & 1)) v = 32;
     return v;
   }();
   return cached;

@@ -35,23 +35,35 @@ namespace {
 constexpr int kPage = 16;
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kMaxSplitPages = 256;   // page ids of one split staged in LDS
+
+// 16-byte-chunk swizzle of V row `row` in a wave's LDS slice.  The transpose
+// read takes 8 consecutive rows x 32 bytes per half-wave; XOR-ing the chunk
+// pair index spreads those rows over distinct bank groups.  Rows r and r+16
+// (the same slot of the two pages of a pair) share the swizzle.
+template <int D>
+__device__ __forceinline__ int dv_swz(int row) {
+  return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
+}
 
 template <int D>
-__global__ __launch_bounds__(kThreads)
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kpool,
                          const bf16* __restrict__ vpool, const int32_t* __restrict__ block_table,
                          const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
                          float* __restrict__ lse_part, int Hq, int Hkv, int num_pages,
                          int max_blocks, int split_pages, int max_splits, float scale_log2) {
-  constexpr int LDV = D + 8;                  // padded LDS row, bf16 elements
-  constexpr int WAVE_LDS = 2 * kPage * LDV;   // one page pair, row-major [32][LDV]
+  constexpr int WAVE_LDS = 2 * kPage * D;     // one page pair, [32 rows][D], swizzled
   constexpr int NDC = D / 32;                 // k-chunks of the S^T MFMA
   constexpr int NDB = D / 16;                 // 16-row blocks of O^T
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
   constexpr int VCH = 2 * kPage * CPR / 64;   // V chunks per lane per pair
   constexpr int RED_STRIDE = D + 4;           // fp32 row stride of the merge buffer
 
+  // LDS: [4 wave slices of V][page ids of this split]; the merge buffer of
+  // the epilogue reuses the V slices.
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  int32_t* pages = reinterpret_cast<int32_t*>(smem + kWaves * WAVE_LDS);
 
   const int split = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
   int len = seq_lens[n];
@@ -60,12 +72,18 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
   if (blk0 * kPage >= len) return;            // whole workgroup: nothing in this split
   const int nblk = (len + kPage - 1) / kPage;
   const int blk_end = min(blk0 + split_pages, nblk);
-  const int npairs = (blk_end - blk0 + 1) >> 1;
+  const int nb = blk_end - blk0;              // blocks of this split
+  const int npairs = (nb + 1) >> 1;
 
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int32_t* bt = block_table + (size_t)n * max_blocks;
+
+  // page ids of the whole split, once (-1 marks a block outside [0, num_pages))
+  for (int i = tid; i < nb; i += kThreads) {
+    const int p = block_table[(size_t)n * max_blocks + blk0 + i];
+    pages[i] = (p >= 0 && p < num_pages) ? p : -1;
+  }
 
   // Q operand (B of S^T = K Q^T): column l16 = query head hk*G + l16.
   bf16x8 qop[NDC];
@@ -77,6 +95,7 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
 #pragma unroll
     for (int c = 0; c < NDC; ++c) qop[c] = bf16x8{};
   }
+  __syncthreads();
 
   float m_run = -INFINITY, l_part = 0.f;
   f32x4 acc[NDB];
@@ -87,51 +106,55 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
   const size_t page_stride = (size_t)Hkv * kPage * D;     // elements per page
   const size_t head_off = (size_t)hk * kPage * D;
 
-  for (int pi = wave; pi < npairs; pi += kWaves) {
-    const int b0 = blk0 + 2 * pi;
-    int pg[2];
-    bool ok[2];
-    pg[0] = bt[b0];
-    ok[0] = pg[0] >= 0 && pg[0] < num_pages;
-    const bool has1 = b0 + 1 < blk_end;
-    pg[1] = has1 ? bt[b0 + 1] : 0;
-    ok[1] = has1 && pg[1] >= 0 && pg[1] < num_pages;
+  // transpose-read address of this lane inside a slice (page 0; +16 rows for page 1)
+  const int vrow = 4 * g + (l16 >> 2);
+  const int vsw = dv_swz<D>(vrow);
+  const bf16* vrd = vl + vrow * D + 4 * (l16 & 1);
+  const int vchunk = (l16 & 3) >> 1;
 
-    // K rows -> registers (A of S^T): lane key l16, d = 32c + 8g .. +7
-    bf16x8 kop[2][NDC];
+  // Loads of one page pair into registers: K as MFMA A-operands (lane key
+  // l16, d = 32c + 8g..+7), V as coalesced 16-byte row chunks.  The loads are
+  // unconditional so that each page needs one base address: a block without a
+  // valid page reads page 0 instead (in bounds), and its scores are masked and
+  // its V rows zeroed before use, like the slots at or past the length.
+  auto page_of = [&](int blk) { return blk < nb ? max(pages[blk], 0) : 0; };
+  auto issue_k = [&](int pi, bf16x8 (&kop)[2][NDC]) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      if (ok[p]) {
-        const bf16* kp = kpool + (size_t)pg[p] * page_stride + head_off + l16 * D + 8 * g;
+      const bf16* kp = kpool + (size_t)page_of(2 * pi + p) * page_stride + head_off + l16 * D + 8 * g;
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) kop[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
-      } else {
+      for (int c = 0; c < NDC; ++c) kop[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
+    }
+  };
+  auto issue_v = [&](int pi, u32x4 (&vreg)[VCH]) {
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) kop[p][c] = bf16x8{};
+    for (int p = 0; p < 2; ++p) {
+      const bf16* vp = vpool + (size_t)page_of(2 * pi + p) * page_stride + head_off + lane * 8;
+#pragma unroll
+      for (int r = 0; r < VCH / 2; ++r) vreg[p * (VCH / 2) + r] = load16(vp + 64 * 8 * r);
+    }
+  };
+  auto block_ok = [&](int blk) { return blk < nb && pages[blk] >= 0; };
+  // V chunk r of page p is row (lane + 64 r) / CPR of that page
+  auto write_v = [&](int pi, const u32x4 (&vreg)[VCH]) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = block_ok(2 * pi + p);
+#pragma unroll
+      for (int r = 0; r < VCH / 2; ++r) {
+        const int c = lane + 64 * r;
+        const int slot = c / CPR, col = c % CPR;
+        const int row = 16 * p + slot;
+        const bool live = ok && (blk0 + 2 * pi + p) * kPage + slot < len;
+        const u32x4 zero = {0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(vl + row * D + (col ^ dv_swz<D>(row)) * 8) =
+            live ? vreg[p * (VCH / 2) + r] : zero;
       }
     }
-    // V rows -> registers (coalesced 16-byte chunks), then row-major into LDS.
-    // Rows at or past the length are zero: their weight is 0, and 0 * NaN
-    // from a stale slot would otherwise poison the MFMA sum.
-    u32x4 vreg[VCH];
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = lane + 64 * r;
-      const int row = c / CPR, col = c % CPR;     // row 0..31: page row>>4, slot row&15
-      const int p = row >> 4;
-      if (ok[p] && (b0 + p) * kPage + (row & 15) < len) {
-        vreg[r] = load16(vpool + (size_t)pg[p] * page_stride + head_off + (row & 15) * D + col * 8);
-      } else {
-        vreg[r] = u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < VCH; ++r) {
-      const int c = lane + 64 * r;
-      const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(vl + row * LDV + col * 8) = vreg[r];
-    }
+  };
 
+  auto compute = [&](int pi, const bf16x8 (&kop)[2][NDC]) {
+    const int bl = 2 * pi;
     // S^T[key][head] for both pages
     f32x4 s[2];
 #pragma unroll
@@ -142,18 +165,17 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
     }
     // mask positions past the length and blocks without a valid page
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 2; ++p) {
+      const bool ok = block_ok(bl + p);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int tok = (b0 + p) * kPage + 4 * g + i;
-        if (!ok[p] || tok >= len) s[p][i] = -INFINITY;
+        const int tok = (blk0 + bl + p) * kPage + 4 * g + i;
+        if (!ok || tok >= len) s[p][i] = -INFINITY;
       }
+    }
 
-    float mx = -INFINITY;
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmax2(mx, s[p][i]);
+    float mx = fmax2(fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3])),
+                     fmax2(fmax2(s[1][0], s[1][1]), fmax2(s[1][2], s[1][3])));
     mx = fmax2(mx, xor_lane(mx, 16));
     mx = fmax2(mx, xor_lane(mx, 32));
     const float m_new = fmax2(m_run, mx * scale_log2);
@@ -179,17 +201,17 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
     const bf16x8 pop = pack_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3],
                                    s[1][0], s[1][1], s[1][2], s[1][3]);
 
-    // the LDS writes above must land before other lanes of this wave read them
+    // the LDS writes of this pair must land before other lanes read them
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     // V^T operand: lane group g reads keys 4g..4g+3 of each page, d = 16db + l16
-    const bf16* vp = vl + (4 * g + (l16 >> 2)) * LDV + 4 * (l16 & 3);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const i16x4 lo = lds_read_tr16(vp + 16 * db);
-      const i16x4 hi4 = lds_read_tr16(vp + kPage * LDV + 16 * db);
+      const int off = ((2 * db + vchunk) ^ vsw) * 8;
+      const i16x4 lo = lds_read_tr16(vrd + off);
+      const i16x4 hi4 = lds_read_tr16(vrd + kPage * D + off);
       acc[db] = mfma_16x16x32(concat_tr(lo, hi4), pop, acc[db]);
     }
 
@@ -197,6 +219,32 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // Software pipeline: K has two register sets, V one (it moves to LDS at the
+  // top of each step, after which its registers take the next pair's V).
+  // The loads of pair pi + 4 are in flight while pair pi is computed.
+  bf16x8 ka[2][NDC], kb[2][NDC];
+  u32x4 vreg[VCH];
+  if (wave < npairs) {
+    issue_k(wave, ka);
+    issue_v(wave, vreg);
+  }
+  for (int pi = wave; pi < npairs; pi += 2 * kWaves) {
+    write_v(pi, vreg);
+    const bool more1 = pi + kWaves < npairs;
+    if (more1) {
+      issue_k(pi + kWaves, kb);
+      issue_v(pi + kWaves, vreg);
+    }
+    compute(pi, ka);
+    if (!more1) break;
+    write_v(pi + kWaves, vreg);
+    if (pi + 2 * kWaves < npairs) {
+      issue_k(pi + 2 * kWaves, ka);
+      issue_v(pi + 2 * kWaves, vreg);
+    }
+    compute(pi + kWaves, kb);
   }
 
   // ---- merge the 4 waves of this split through LDS ----
@@ -246,6 +294,9 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
   }
 }
 
+// One wave per (sequence, head): lane s holds split s's log-sum-exp (splits
+// beyond 64 are folded in a loop), the wave reduces max and sum, then each
+// lane accumulates D/64 output elements over the splits.
 template <int D>
 __global__ __launch_bounds__(64)
 void decode_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
@@ -255,6 +306,7 @@ void decode_combine_kernel(const float* __restrict__ o_part, const float* __rest
   constexpr int PER = D / 64;
   const int nh = blockIdx.x;
   const int n = nh / Hq;
+  const int lane = threadIdx.x;
   int len = seq_lens[n];
   len = max(0, min(len, max_blocks * kPage));
   const int nsplit = (len + split_pages * kPage - 1) / (split_pages * kPage);
@@ -262,23 +314,43 @@ void decode_combine_kernel(const float* __restrict__ o_part, const float* __rest
   const float* op = o_part + (size_t)nh * max_splits * D;
 
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) M = fmax2(M, lp[s]);
+  for (int s = lane; s < nsplit; s += 64) M = fmax2(M, lp[s]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmax2(M, xor_lane(M, m));
+  float W = 0.f;
+  if (M != -INFINITY)
+    for (int s = lane; s < nsplit; s += 64) W += expf(lp[s] - M);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) W += xor_lane(W, m);
+
   float out[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[e] = 0.f;
-  float W = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float w = expf(lp[s] - M);
-      W += w;
+  if (W > 0.f) {
+    int s = 0;
+    for (; s + 4 <= nsplit; s += 4) {
+      float w[4], x[4][PER];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(w, op[(size_t)s * D + threadIdx.x * PER + e], out[e]);
+      for (int u = 0; u < 4; ++u) {
+        w[u] = expf(lp[s + u] - M);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x[u][e] = op[(size_t)(s + u) * D + lane * PER + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(w[u], x[u][e], out[e]);
+    }
+    for (; s < nsplit; ++s) {
+      const float w = expf(lp[s] - M);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(w, op[(size_t)s * D + lane * PER + e], out[e]);
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[(size_t)nh * D + threadIdx.x * PER + e] = (bf16)(out[e] * inv);
-  if (lse != nullptr && threadIdx.x == 0) lse[nh] = W > 0.f ? M + logf(W) : -INFINITY;
+  for (int e = 0; e < PER; ++e) o[(size_t)nh * D + lane * PER + e] = (bf16)(out[e] * inv);
+  if (lse != nullptr && lane == 0) lse[nh] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 template <int D>
@@ -287,7 +359,7 @@ hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
                     float* o_part, float* lse_part, int N, int Hq, int Hkv, int num_pages,
                     int max_blocks, int split_pages, int max_splits, float scale_log2,
                     hipStream_t stream) {
-  constexpr size_t v_lds = (size_t)kWaves * 2 * kPage * (D + 8) * sizeof(bf16);
+  constexpr size_t v_lds = (size_t)kWaves * 2 * kPage * D * sizeof(bf16) + kMaxSplitPages * 4;
   constexpr size_t red_lds = ((size_t)kWaves * 16 * (D + 4) + 2 * kWaves * 16) * sizeof(float);
   constexpr size_t smem = v_lds > red_lds ? v_lds : red_lds;
   const int nsplit_grid = (max_blocks + split_pages - 1) / split_pages;

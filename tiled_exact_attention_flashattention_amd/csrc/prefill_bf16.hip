@@ -42,6 +42,16 @@ namespace {
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kThreads = 256; // 4 waves
 
+// 16-byte-chunk swizzle of V row `row`: the transpose read touches 4
+// consecutive rows x 64 bytes at once; XOR-ing the chunk index puts those rows
+// in different bank groups (a row of D=128 spans all 64 banks, one of D=64
+// half of them).  Depends on row bits 0-1 only, so it is the same for rows
+// 16c + r and 16c + 8 + r.
+template <int D>
+__device__ __forceinline__ int v_swz_of(int row) {
+  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
+}
+
 template <int D> struct PrefillTile;
 template <> struct PrefillTile<128> { static constexpr int BN = 64; };
 template <> struct PrefillTile<64> { static constexpr int BN = 128; };
@@ -53,8 +63,10 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
                          float scale_log2) {
   constexpr int BN = PrefillTile<D>::BN;
-  constexpr int LDK = D + 8;                 // padded LDS row, bf16 elements
-  constexpr int TILE = BN * LDK;             // one K (or V) tile in LDS
+  constexpr int LDK = D + 8;                 // padded K row in LDS, bf16 elements
+  constexpr int KTILE = BN * LDK;            // one K tile in LDS
+  constexpr int VTILE = BN * D;              // one V tile in LDS (unpadded, swizzled)
+  constexpr int STAGE = KTILE + VTILE;
   constexpr int NKB = BN / 32;               // 32-key blocks of S^T
   constexpr int NDC = D / 16;                // k-chunks of the S^T MFMA
   constexpr int NDB = D / 32;                // 32-row blocks of O^T
@@ -62,8 +74,13 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int CPT = BN * CPR / kThreads;   // chunks per thread per tile
   static_assert(CPT * kThreads == BN * CPR, "tile must split evenly");
+  auto v_swz = [](int row) { return v_swz_of<D>(row); };
 
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [2 stages][K,V][BN][LDK]
+  // LDS: 2 stages of [K tile (padded rows) | V tile (rows of D, 16-byte chunks
+  // XOR-swizzled per row)].  K is read 16 rows x 16 bytes per bank cycle, which
+  // the 16-byte row pad spreads over all banks; V is read by the transpose
+  // read as 4 consecutive rows x 64 bytes, which the swizzle spreads instead.
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
 
   // ---- which (q tile, batch, head) this workgroup computes ----
   const int ntq = (T + kBM - 1) / kBM;
@@ -139,14 +156,14 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
   auto store_tile = [&](int stage) {
-    bf16* ks = smem + stage * 2 * TILE;
-    bf16* vs = ks + TILE;
+    bf16* ks = smem + stage * STAGE;
+    bf16* vs = ks + KTILE;
 #pragma unroll
     for (int r = 0; r < CPT; ++r) {
       const int c = tid + kThreads * r;
       const int row = c / CPR, col = c % CPR;
       *reinterpret_cast<u32x4*>(ks + row * LDK + col * 8) = kr[r];
-      *reinterpret_cast<u32x4*>(vs + row * LDK + col * 8) = vr[r];
+      *reinterpret_cast<u32x4*>(vs + row * D + (col ^ v_swz(row)) * 8) = vr[r];
     }
   };
 
@@ -158,10 +175,16 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
 
   // transpose-read addressing of V (see cdna4.hpp): lane group G = lane/16
-  // covers rows d = 32*db + 16*(G&1) + lane%16 and key group hi = G>>1.
+  // covers rows d = 32*db + 16*(G&1) + lane%16 and key group hi = G>>1.  The
+  // key row of this lane is 16*c + v_row_off (+8 for the second read); the
+  // swizzle depends only on row bits that c and the +8 do not touch.
   const int g16 = lane >> 4, j16 = lane & 15;
   const int v_row_off = 4 * hi + (j16 >> 2);                  // key within a 16-key chunk
-  const int v_col_off = 16 * (g16 & 1) + 4 * (j16 & 3);       // d within a 32-row block
+  // d of this lane's 8-byte row piece: 32*db + 16*(G&1) + 4*(j16&3), i.e.
+  // 16-byte chunk 4*db + v_chunk, element v_in inside it
+  const int v_chunk = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int v_in = 4 * (j16 & 1);
+  const int v_sw = v_swz(v_row_off);
 
   load_tile(0);
   store_tile(0);
@@ -172,20 +195,32 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (j + 1 < ntk) load_tile(j + 1);
 
     if (wave_live && j * BN < wave_kv_end) {
-      const bf16* ks = smem + stage * 2 * TILE;
-      const bf16* vs = ks + TILE;
+      const bf16* ks = smem + stage * STAGE;
+      const bf16* vs = ks + KTILE;
 
-      // S^T[key][row] for the BN keys of this tile
+      // S^T[key][row] for the BN keys of this tile.  The K operands of
+      // d-chunk c+1 are read from LDS while the MFMAs of chunk c run, and the
+      // NKB independent accumulators alternate so that dependent MFMAs are
+      // not issued back to back.
       f32x16 s[NKB];
+      const bf16* kp = ks + l32 * LDK + 8 * hi;
+      bf16x8 kcur[NKB], knext[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         s[kb] = f32x16{};
-        const bf16* kp = ks + (32 * kb + l32) * LDK + 8 * hi;
+        kcur[kb] = *reinterpret_cast<const bf16x8*>(kp + 32 * kb * LDK);
+      }
 #pragma unroll
-        for (int c = 0; c < NDC; ++c) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(kp + 16 * c);
-          s[kb] = mfma_32x32x16(kop, qop[c], s[kb]);
+      for (int c = 0; c < NDC; ++c) {
+        if (c + 1 < NDC) {
+#pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            knext[kb] = *reinterpret_cast<const bf16x8*>(kp + 32 * kb * LDK + 16 * (c + 1));
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma_32x32x16(kcur[kb], qop[c], s[kb]);
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) kcur[kb] = knext[kb];
       }
 
       // mask keys past the diagonal or past S (only tiles that need it)
@@ -233,11 +268,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int o8 = 8 * (c & 1);
         const bf16x8 pop = pack_bf16x8(sp[o8 + 0], sp[o8 + 1], sp[o8 + 2], sp[o8 + 3],
                                        sp[o8 + 4], sp[o8 + 5], sp[o8 + 6], sp[o8 + 7]);
-        const bf16* vp = vs + (16 * c + v_row_off) * LDK + v_col_off;
+        const bf16* vp = vs + (16 * c + v_row_off) * D + v_in;
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-          const i16x4 lo = lds_read_tr16(vp + 32 * db);
-          const i16x4 hi4 = lds_read_tr16(vp + 8 * LDK + 32 * db);
+          const int off = ((4 * db + v_chunk) ^ v_sw) * 8;
+          const i16x4 lo = lds_read_tr16(vp + off);
+          const i16x4 hi4 = lds_read_tr16(vp + 8 * D + off);
           acc[db] = mfma_32x32x16(concat_tr(lo, hi4), pop, acc[db]);
         }
       }
@@ -272,7 +308,7 @@ template <int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
   constexpr int BN = PrefillTile<D>::BN;
-  constexpr size_t smem = 2 * 2 * (size_t)BN * (D + 8) * sizeof(bf16);
+  constexpr size_t smem = 2 * (size_t)BN * ((D + 8) + D) * sizeof(bf16);
   static bool attr_set = false;   // benign race: the attribute is idempotent
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, CAUSAL>,
