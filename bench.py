@@ -178,7 +178,9 @@ def main():
     do = torch.empty_like(dq)
     dlse = torch.empty((dinp.N, dinp.Hq), dtype=torch.float32, device=dev)
     ws = tea.decode_workspace(dinp.N, dinp.Hq, dinp.d, dinp.max_blocks, dev)
-    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.int32, device=dev)
+    # float32 so that sum() only reads it (an int32 sum would first write an
+    # int64 copy, leaving dirty cache lines whose write-back slows the kernels)
+    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
 
     stream = torch.cuda.current_stream(dev)
     events = []

@@ -223,28 +223,29 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
 
   // Software pipeline: K has two register sets, V one (it moves to LDS at the
   // top of each step, after which its registers take the next pair's V).
-  // The loads of pair pi + 4 are in flight while pair pi is computed.
+  // The loads of pair pi + 4 are in flight while pair pi is computed.  Every
+  // load is issued unconditionally -- past the last pair the index is clamped,
+  // re-reading that pair from L2 -- so the number of loads in flight is the
+  // same on every path and the compiler's wait counts stay exact; a load
+  // behind a branch would make it wait for the prefetched pair as well.
   bf16x8 ka[2][NDC], kb[2][NDC];
   u32x4 vreg[VCH];
   if (wave < npairs) {
+    auto clampp = [&](int pi) { return min(pi, npairs - 1); };
     issue_k(wave, ka);
     issue_v(wave, vreg);
-  }
-  for (int pi = wave; pi < npairs; pi += 2 * kWaves) {
-    write_v(pi, vreg);
-    const bool more1 = pi + kWaves < npairs;
-    if (more1) {
-      issue_k(pi + kWaves, kb);
-      issue_v(pi + kWaves, vreg);
+    for (int pi = wave;; pi += 2 * kWaves) {
+      write_v(pi, vreg);
+      issue_k(clampp(pi + kWaves), kb);
+      issue_v(clampp(pi + kWaves), vreg);
+      compute(pi, ka);
+      if (pi + kWaves >= npairs) break;
+      write_v(pi + kWaves, vreg);
+      issue_k(clampp(pi + 2 * kWaves), ka);
+      issue_v(clampp(pi + 2 * kWaves), vreg);
+      compute(pi + kWaves, kb);
+      if (pi + 2 * kWaves >= npairs) break;
     }
-    compute(pi, ka);
-    if (!more1) break;
-    write_v(pi + kWaves, vreg);
-    if (pi + 2 * kWaves < npairs) {
-      issue_k(pi + 2 * kWaves, ka);
-      issue_v(pi + 2 * kWaves, vreg);
-    }
-    compute(pi + kWaves, kb);
   }
 
   // ---- merge the 4 waves of this split through LDS ----

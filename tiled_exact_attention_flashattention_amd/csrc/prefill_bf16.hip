@@ -14,22 +14,22 @@
 //
 // gfx950 mapping:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, query head);
-//     each wave owns 32 rows and keeps its Q rows in registers as MFMA
-//     B-operands for the whole kernel;
-//   * K and V tiles of BN keys are staged HBM -> registers -> LDS, double
-//     buffered: the global loads of tile j+1 are in flight while tile j is
-//     computed, and one barrier per tile separates the LDS phases;
-//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: lane l ends up holding 16 keys
-//     of query row l%32 per 32-key block, so the row max needs one exchange
-//     with lane l^32 and the row sum none until the end;
-//   * the exponentiated scores are rounded to bf16 and used in place as the
-//     B-operand of O^T = V^T P^T (same MFMA shape), with V^T read from the
-//     row-major V tile by the gfx950 LDS transpose read; O^T's accumulator has
-//     the same query-per-lane layout, so the rescale by exp2(m_old - m_new)
-//     is a per-lane multiply;
+//     each wave owns 32 rows as two 16-row blocks and keeps their Q in
+//     registers as MFMA B-operands for the whole kernel;
+//   * K and V tiles of BN keys go HBM -> LDS by the gfx950 direct-to-LDS load
+//     (no register staging), into two stages held in separate LDS objects:
+//     the load of tile j+1 runs while tile j is computed, one barrier per
+//     tile, with the vmcnt waits placed by hand;
+//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_16x16x32_bf16: a lane holds
+//     4 keys of one query row per 16-key block, and the exponentiated scores
+//     of two adjacent blocks are exactly the P operand of one P.V MFMA; V^T
+//     comes from the row-major V tile through the LDS transpose read; every K
+//     and V operand read from LDS feeds the MFMAs of both row blocks;
+//   * K and V tiles are stored unpadded with their 16-byte chunks XOR-swizzled
+//     per row so that both operand read patterns are bank-conflict free;
 //   * causal: K/V tiles past the workgroup's last visible key are never
-//     loaded, a wave skips the MFMA work of tiles it cannot see, and only
-//     tiles crossing the diagonal (or the ragged end) pay for the mask;
+//     loaded, a wave skips tiles it cannot see, and only tiles crossing the
+//     diagonal (or the ragged end) pay for the mask;
 //   * heavy causal tiles are dispatched first, and when the number of
 //     (batch, KV head) groups is a multiple of 8 every group stays on one XCD
 //     so its K/V is re-read from that XCD's L2.
@@ -42,19 +42,49 @@ namespace {
 constexpr int kBM = 128;      // query rows per workgroup
 constexpr int kThreads = 256; // 4 waves
 
-// 16-byte-chunk swizzle of V row `row`: the transpose read touches 4
-// consecutive rows x 64 bytes at once; XOR-ing the chunk index puts those rows
-// in different bank groups (a row of D=128 spans all 64 banks, one of D=64
-// half of them).  Depends on row bits 0-1 only, so it is the same for rows
-// 16c + r and 16c + 8 + r.
-template <int D>
-__device__ __forceinline__ int v_swz_of(int row) {
-  return D == 128 ? 4 * (row & 3) : 4 * ((row >> 1) & 1);
-}
-
 template <int D> struct PrefillTile;
 template <> struct PrefillTile<128> { static constexpr int BN = 64; };
 template <> struct PrefillTile<64> { static constexpr int BN = 128; };
+
+// Chunk swizzles (16-byte chunks within a row of D bf16).
+// K is read as 16 rows x one chunk per 16 lanes: spread the 16 rows over all
+// banks.  V is read by the transpose read as 8 rows x 32 bytes per half-wave:
+// spread those 8 rows.  A row of D=128 spans the 64 banks once, a row of D=64
+// half of them, hence the different row bits.
+template <int D>
+__device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : ((row >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
+
+// s_waitcnt encoding (gfx9): vmcnt(0) lgkmcnt(0), expcnt unconstrained.
+constexpr unsigned kWaitVm0Lgkm0 = 0x0070;
+
+// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from `gptr` land
+// at LDS byte address `lds_base` + 16 i (lds_base wave-uniform, in M0).
+// Issued through asm so that the compiler does not track it: its own wait
+// insertion would otherwise stall the LDS transpose reads of the current stage
+// until this load, aimed at the other stage, completed.  Completion is awaited
+// explicitly (vmcnt) before the barrier that publishes the stage.  M0 has no
+// other user in this kernel (no compiler-issued LDS DMA, no indirect register
+// indexing, no messages), so setting it here disturbs nothing.
+__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(gptr), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Workgroup barrier without a memory fence: the LDS stages are filled by the
+// direct-to-LDS loads, whose completion is awaited explicitly with vmcnt, and
+// a fence here would make the compiler wait for the load in flight as well.
+// The empty asm statements keep the optimiser from moving LDS accesses across.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
@@ -63,24 +93,20 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
                          float scale_log2) {
   constexpr int BN = PrefillTile<D>::BN;
-  constexpr int LDK = D + 8;                 // padded K row in LDS, bf16 elements
-  constexpr int KTILE = BN * LDK;            // one K tile in LDS
-  constexpr int VTILE = BN * D;              // one V tile in LDS (unpadded, swizzled)
-  constexpr int STAGE = KTILE + VTILE;
-  constexpr int NKB = BN / 32;               // 32-key blocks of S^T
-  constexpr int NDC = D / 16;                // k-chunks of the S^T MFMA
-  constexpr int NDB = D / 32;                // 32-row blocks of O^T
-  constexpr int NPC = BN / 16;               // k-chunks of the P.V MFMA
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
-  constexpr int CPT = BN * CPR / kThreads;   // chunks per thread per tile
-  static_assert(CPT * kThreads == BN * CPR, "tile must split evenly");
-  auto v_swz = [](int row) { return v_swz_of<D>(row); };
+  constexpr int NKB = BN / 16;               // 16-key blocks of S^T
+  constexpr int NDC = D / 32;                // k-chunks of the S^T MFMA
+  constexpr int NDB = D / 16;                // 16-row blocks of O^T
+  constexpr int NPC = BN / 32;               // 32-key chunks of the P.V MFMA
+  constexpr int CPW = BN * CPR / kThreads;   // direct-to-LDS loads per thread per tile (K, and V)
+  static_assert(CPW * kThreads == BN * CPR, "tile must split evenly");
 
-  // LDS: 2 stages of [K tile (padded rows) | V tile (rows of D, 16-byte chunks
-  // XOR-swizzled per row)].  K is read 16 rows x 16 bytes per bank cycle, which
-  // the 16-byte row pad spreads over all banks; V is read by the transpose
-  // read as 4 consecutive rows x 64 bytes, which the swizzle spreads instead.
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  // two stages, each K and V in its own object so that the compiler can tell
+  // the stage being read from the one being loaded
+  __shared__ __attribute__((aligned(16))) bf16 k_st0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 v_st0[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 k_st1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 v_st1[BN * D];
 
   // ---- which (q tile, batch, head) this workgroup computes ----
   const int ntq = (T + kBM - 1) / kBM;
@@ -108,7 +134,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hi = lane >> 5;
+  const int l16 = lane & 15, g = lane >> 4;
 
   const size_t qbase = ((size_t)(b * Hq + h) * T) * D;
   const size_t kvbase = ((size_t)(b * Hkv + hk) * S) * D;
@@ -123,202 +149,188 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
   const int ntk = (wg_kv_end + BN - 1) / BN;
 
+  // ---- direct-to-LDS tile load ----
+  // Instruction r of wave w fills LDS chunks [64 (w CPW + r), +64): lane l
+  // writes chunk p = 64 (w CPW + r) + l, i.e. row p / CPR, physical chunk
+  // p % CPR, which holds logical chunk (p % CPR) ^ swz(row).  Rows past S
+  // re-read row S-1 (in bounds; their scores are masked and their weights 0).
+  auto load_tile = [&](int j, bf16* ks, bf16* vs) {
+#pragma unroll
+    for (int r = 0; r < CPW; ++r) {
+      const int blk = wave * CPW + r;
+      const int p = 64 * blk + lane;
+      const int row = p / CPR, cph = p % CPR;
+      const int key = min(j * BN + row, S - 1);
+      const bf16* krow = k + kvbase + (size_t)key * D;
+      const bf16* vrow = v + kvbase + (size_t)key * D;
+      lds_dma16(krow + (cph ^ k_swz<D>(row)) * 8, __builtin_amdgcn_readfirstlane(lds_addr(ks + 512 * blk)));
+      lds_dma16(vrow + (cph ^ v_swz<D>(row)) * 8, __builtin_amdgcn_readfirstlane(lds_addr(vs + 512 * blk)));
+    }
+  };
+
   // ---- Q rows into registers (B operand of S^T = K Q^T) ----
-  const int qrow = wrow0 + l32;
-  bf16x8 qop[NDC];
-  if (qrow < T) {
-    const bf16* qp = q + qbase + (size_t)qrow * D + 8 * hi;
+  bf16x8 qop[2][NDC];
+  int row_lim[2];
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qp + 16 * c);
-  } else {
+  for (int qb = 0; qb < 2; ++qb) {
+    const int row = wrow0 + 16 * qb + l16;
+    if (row < T) {
+      const bf16* qp = q + qbase + (size_t)row * D + 8 * g;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) qop[c] = bf16x8{};
+      for (int c = 0; c < NDC; ++c) qop[qb][c] = *reinterpret_cast<const bf16x8*>(qp + 32 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) qop[qb][c] = bf16x8{};
+    }
+    // last key visible to this row (rows past T only feed discarded lanes)
+    row_lim[qb] = CAUSAL ? min(row + (S - T), S - 1) : S - 1;
   }
-  // last key visible to this lane's row (rows past T only feed discarded lanes)
-  const int row_lim = CAUSAL ? min(qrow + (S - T), S - 1) : S - 1;
 
-  // ---- tile staging ----
-  u32x4 kr[CPT], vr[CPT];
-  auto load_tile = [&](int j) {
+  // ---- running softmax state of rows wrow0 + 16 qb + l16 ----
+  float m_run[2] = {-INFINITY, -INFINITY};   // running max of scaled logits, log2 units
+  float l_part[2] = {0.f, 0.f};              // sum over this lane's keys of exp2(s - m_run)
+  f32x4 acc[2][NDB];
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / CPR, col = c % CPR;
-      const int key = j * BN + row;
-      if (key < S) {
-        const size_t off = kvbase + (size_t)key * D + col * 8;
-        kr[r] = load16(k + off);
-        vr[r] = load16(v + off);
-      } else {
-        kr[r] = u32x4{0, 0, 0, 0};
-        vr[r] = u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto store_tile = [&](int stage) {
-    bf16* ks = smem + stage * STAGE;
-    bf16* vs = ks + KTILE;
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-    for (int r = 0; r < CPT; ++r) {
-      const int c = tid + kThreads * r;
-      const int row = c / CPR, col = c % CPR;
-      *reinterpret_cast<u32x4*>(ks + row * LDK + col * 8) = kr[r];
-      *reinterpret_cast<u32x4*>(vs + row * D + (col ^ v_swz(row)) * 8) = vr[r];
-    }
-  };
+    for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{};
 
-  // ---- running softmax state of row qrow (replicated in lanes l, l^32) ----
-  float m_run = -INFINITY;   // running max of scaled logits, log2 units
-  float l_part = 0.f;        // sum over this lane's keys of exp2(s - m_run)
-  f32x16 acc[NDB];
+  // per-lane operand addressing inside a stage
+  const int kswz = k_swz<D>(l16);                             // same for row 16 kb + l16
+  const int v_row = 4 * g + (l16 >> 2);                       // key within a 32-key chunk
+  const int v_chunk = (l16 & 3) >> 1;                         // + 2 db
+  const int v_sw = v_swz<D>(v_row);                           // same for v_row + 16, + 32 c
+  const int v_in = 4 * (l16 & 1);
+
+  auto compute_tile = [&](int j, const bf16* ks, const bf16* vs) {
+    // S^T[key][row] for the BN keys of this tile; each K operand feeds both row blocks
+    f32x4 s[2][NKB];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x16{};
-
-  // transpose-read addressing of V (see cdna4.hpp): lane group G = lane/16
-  // covers rows d = 32*db + 16*(G&1) + lane%16 and key group hi = G>>1.  The
-  // key row of this lane is 16*c + v_row_off (+8 for the second read); the
-  // swizzle depends only on row bits that c and the +8 do not touch.
-  const int g16 = lane >> 4, j16 = lane & 15;
-  const int v_row_off = 4 * hi + (j16 >> 2);                  // key within a 16-key chunk
-  // d of this lane's 8-byte row piece: 32*db + 16*(G&1) + 4*(j16&3), i.e.
-  // 16-byte chunk 4*db + v_chunk, element v_in inside it
-  const int v_chunk = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  const int v_in = 4 * (j16 & 1);
-  const int v_sw = v_swz(v_row_off);
-
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntk; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < ntk) load_tile(j + 1);
-
-    if (wave_live && j * BN < wave_kv_end) {
-      const bf16* ks = smem + stage * STAGE;
-      const bf16* vs = ks + KTILE;
-
-      // S^T[key][row] for the BN keys of this tile.  The K operands of
-      // d-chunk c+1 are read from LDS while the MFMAs of chunk c run, and the
-      // NKB independent accumulators alternate so that dependent MFMAs are
-      // not issued back to back.
-      f32x16 s[NKB];
-      const bf16* kp = ks + l32 * LDK + 8 * hi;
-      bf16x8 kcur[NKB], knext[NKB];
+    for (int kb = 0; kb < NKB; ++kb) s[0][kb] = s[1][kb] = f32x4{};
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        kcur[kb] = *reinterpret_cast<const bf16x8*>(kp + 32 * kb * LDK);
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(
+            ks + (16 * kb + l16) * D + (((4 * c + g) ^ kswz) * 8));
+        s[0][kb] = mfma_16x16x32(kop, qop[0][c], s[0][kb]);
+        s[1][kb] = mfma_16x16x32(kop, qop[1][c], s[1][kb]);
       }
-#pragma unroll
-      for (int c = 0; c < NDC; ++c) {
-        if (c + 1 < NDC) {
-#pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            knext[kb] = *reinterpret_cast<const bf16x8*>(kp + 32 * kb * LDK + 16 * (c + 1));
-        }
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) s[kb] = mfma_32x32x16(kcur[kb], qop[c], s[kb]);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) kcur[kb] = knext[kb];
-      }
+    }
 
-      // mask keys past the diagonal or past S (only tiles that need it)
-      const bool need_mask = ((j + 1) * BN > S) || (CAUSAL && (j + 1) * BN - 1 > wrow0 + (S - T));
-      if (need_mask) {
+    // mask keys past the diagonal or past S (only tiles that need it)
+    const bool need_mask = ((j + 1) * BN > S) || (CAUSAL && (j + 1) * BN - 1 > wrow0 + (S - T));
+    if (need_mask) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = j * BN + 32 * kb + 8 * (i >> 2) + 4 * hi + (i & 3);
-            if (key > row_lim) s[kb][i] = -INFINITY;
+          for (int i = 0; i < 4; ++i) {
+            const int key = j * BN + 16 * kb + 4 * g + i;
+            if (key > row_lim[qb]) s[qb][kb][i] = -INFINITY;
           }
-      }
+    }
 
-      // online softmax update (base 2)
+    // online softmax update (base 2), per row block
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmax2(mx, s[kb][i]);
+        mx = fmax2(mx, fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), fmax2(s[qb][kb][2], s[qb][kb][3])));
+      mx = fmax2(mx, xor_lane(mx, 16));
       mx = fmax2(mx, xor_lane(mx, 32));
-      const float m_new = fmax2(m_run, mx * scale_log2);
+      const float m_new = fmax2(m_run[qb], mx * scale_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run - m_use);
-      m_run = m_new;
+      const float alpha = exp2_hw(m_run[qb] - m_use);
+      m_run[qb] = m_new;
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = exp2_hw(__builtin_fmaf(s[kb][i], scale_log2, -m_use));
-          s[kb][i] = p;
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -m_use));
+          s[qb][kb][i] = p;
           rs += p;
         }
-      l_part = __builtin_fmaf(l_part, alpha, rs);
+      l_part[qb] = __builtin_fmaf(l_part[qb], alpha, rs);
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
-
-      // O^T += V^T P^T, 16 keys at a time
-#pragma unroll
-      for (int c = 0; c < NPC; ++c) {
-        const f32x16& sp = s[c >> 1];
-        const int o8 = 8 * (c & 1);
-        const bf16x8 pop = pack_bf16x8(sp[o8 + 0], sp[o8 + 1], sp[o8 + 2], sp[o8 + 3],
-                                       sp[o8 + 4], sp[o8 + 5], sp[o8 + 6], sp[o8 + 7]);
-        const bf16* vp = vs + (16 * c + v_row_off) * D + v_in;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int off = ((4 * db + v_chunk) ^ v_sw) * 8;
-          const i16x4 lo = lds_read_tr16(vp + off);
-          const i16x4 hi4 = lds_read_tr16(vp + 8 * D + off);
-          acc[db] = mfma_32x32x16(concat_tr(lo, hi4), pop, acc[db]);
-        }
-      }
+        for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha;
     }
 
-    if (j + 1 < ntk) store_tile(stage ^ 1);
-    __syncthreads();
+    // O^T += V^T P^T, 32 keys at a time; each V operand feeds both row blocks
+#pragma unroll
+    for (int c = 0; c < NPC; ++c) {
+      bf16x8 pop[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+        pop[qb] = pack_bf16x8(s[qb][2 * c][0], s[qb][2 * c][1], s[qb][2 * c][2], s[qb][2 * c][3],
+                              s[qb][2 * c + 1][0], s[qb][2 * c + 1][1], s[qb][2 * c + 1][2],
+                              s[qb][2 * c + 1][3]);
+      const bf16* vp = vs + (32 * c + v_row) * D + v_in;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int off = ((2 * db + v_chunk) ^ v_sw) * 8;
+        const i16x4 lo = lds_read_tr16(vp + off);
+        const i16x4 hi4 = lds_read_tr16(vp + 16 * D + off);
+        const bf16x8 vop = concat_tr(lo, hi4);
+        acc[0][db] = mfma_16x16x32(vop, pop[0], acc[0][db]);
+        acc[1][db] = mfma_16x16x32(vop, pop[1], acc[1][db]);
+      }
+    }
+  };
+
+  // One step: wait for this tile's loads, publish it to the workgroup (which
+  // also proves every wave is done with the other stage), start loading the
+  // next tile into the other stage, compute this one.
+  auto step = [&](int j, const bf16* ks, const bf16* vs, bf16* kn, bf16* vn) {
+    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    stage_barrier();
+    if (j + 1 < ntk) load_tile(j + 1, kn, vn);
+    if (wave_live && j * BN < wave_kv_end) compute_tile(j, ks, vs);
+  };
+
+  load_tile(0, k_st0, v_st0);
+  for (int j = 0;;) {
+    step(j, k_st0, v_st0, k_st1, v_st1);
+    if (++j >= ntk) break;
+    step(j, k_st1, v_st1, k_st0, v_st0);
+    if (++j >= ntk) break;
   }
 
   // ---- epilogue: O = acc / l (bf16, nearest even), LSE = ln2 * (m + log2 l) ----
-  const float l_tot = l_part + xor_lane(l_part, 32);
-  if (qrow < T) {
-    const float inv = 1.f / l_tot;
-    bf16* op = o + qbase + (size_t)qrow * D + 4 * hi;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    float l_tot = l_part[qb] + xor_lane(l_part[qb], 16);
+    l_tot += xor_lane(l_tot, 32);
+    const int row = wrow0 + 16 * qb + l16;
+    if (row < T) {
+      const float inv = 1.f / l_tot;
+      bf16* op = o + qbase + (size_t)row * D + 4 * g;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+      for (int db = 0; db < NDB; ++db) {
         bf16x4 r;
-        r[0] = (bf16)(acc[db][4 * jj + 0] * inv);
-        r[1] = (bf16)(acc[db][4 * jj + 1] * inv);
-        r[2] = (bf16)(acc[db][4 * jj + 2] * inv);
-        r[3] = (bf16)(acc[db][4 * jj + 3] * inv);
-        *reinterpret_cast<bf16x4*>(op + 32 * db + 8 * jj) = r;
+        r[0] = (bf16)(acc[qb][db][0] * inv);
+        r[1] = (bf16)(acc[qb][db][1] * inv);
+        r[2] = (bf16)(acc[qb][db][2] * inv);
+        r[3] = (bf16)(acc[qb][db][3] * inv);
+        *reinterpret_cast<bf16x4*>(op + 16 * db) = r;
       }
-    if (lse != nullptr && hi == 0)
-      lse[(size_t)(b * Hq + h) * T + qrow] = (m_run + log2f(l_tot)) * kLn2;
+      if (lse != nullptr && g == 0)
+        lse[(size_t)(b * Hq + h) * T + row] = (m_run[qb] + log2f(l_tot)) * kLn2;
+    }
   }
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
-  constexpr int BN = PrefillTile<D>::BN;
-  constexpr size_t smem = 2 * (size_t)BN * ((D + 8) + D) * sizeof(bf16);
-  static bool attr_set = false;   // benign race: the attribute is idempotent
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_bf16_kernel<D, CAUSAL>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), smem,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S,
                      scale_log2);
