@@ -75,6 +75,35 @@ __device__ __forceinline__ bf16x8 concat_tr(i16x4 lo, i16x4 hi) {
 
 __device__ __forceinline__ float xor_lane(float x, int mask) { return __shfl_xor(x, mask); }
 
+// Pair reductions across lanes l and l^16 (resp. l^32) with the gfx950
+// v_permlane16_swap / v_permlane32_swap VALU ops (no LDS round trip).  Called
+// with the same value in both operands, the swap returns, in every lane, the
+// pair (x[l & ~m], x[l | m]) in that order (checked on the device), so both
+// lanes of a pair compute the same max / sum bit for bit.
+__device__ __forceinline__ float pair_max16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair_sum32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// True in every lane if the predicate holds in any lane of the wave.
+__device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
+
 // Exact-rounding-independent max: both operands are finite or -inf.
 __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_fmaxf(a, b); }
 

@@ -176,11 +176,11 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
 
     float mx = fmax2(fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3])),
                      fmax2(fmax2(s[1][0], s[1][1]), fmax2(s[1][2], s[1][3])));
-    mx = fmax2(mx, xor_lane(mx, 16));
-    mx = fmax2(mx, xor_lane(mx, 32));
+    mx = pair_max32(pair_max16(mx));
     const float m_new = fmax2(m_run, mx * scale_log2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_hw(m_run - m_use);
+    const bool rescale = wave_any(m_new != m_run);
     m_run = m_new;
     float rs = 0.f;
 #pragma unroll
@@ -192,10 +192,12 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
         rs += e;
       }
     l_part = __builtin_fmaf(l_part, alpha, rs);
+    if (rescale) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+    }
 
     // P operand (B of O^T = V^T P^T): slots 0-3 page 0 keys 4g+i, 4-7 page 1
     const bf16x8 pop = pack_bf16x8(s[0][0], s[0][1], s[0][2], s[0][3],
@@ -249,8 +251,7 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
   }
 
   // ---- merge the 4 waves of this split through LDS ----
-  float l_tot = l_part + xor_lane(l_part, 16);
-  l_tot += xor_lane(l_tot, 32);
+  const float l_tot = pair_sum32(pair_sum16(l_part));
   __syncthreads();                                   // all V slices consumed
   float* red_o = reinterpret_cast<float*>(smem);     // [wave][16 heads][RED_STRIDE]
   float* red_m = red_o + kWaves * 16 * RED_STRIDE;   // [wave][16]

@@ -36,15 +36,28 @@
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
+#ifndef PREFILL_D128_WAVES
+#define PREFILL_D128_WAVES 4
+#define PREFILL_D128_BN 64
+#define PREFILL_D128_STAGES 2
+#define PREFILL_D64_WAVES 4
+#define PREFILL_D64_BN 128
+#define PREFILL_D64_STAGES 2
+#endif
+
 namespace attn {
 namespace {
 
-constexpr int kBM = 128;      // query rows per workgroup
-constexpr int kThreads = 256; // 4 waves
-
-template <int D> struct PrefillTile;
-template <> struct PrefillTile<128> { static constexpr int BN = 64; };
-template <> struct PrefillTile<64> { static constexpr int BN = 128; };
+// Tile configuration per head dimension: waves per workgroup (32 query rows
+// each), keys per K/V tile, and LDS stages in the load ring (the load of tile
+// j + STAGES - 1 is in flight while tile j is computed).
+template <int D> struct PrefillCfg;
+template <> struct PrefillCfg<128> {
+  static constexpr int WAVES = PREFILL_D128_WAVES, BN = PREFILL_D128_BN, STAGES = PREFILL_D128_STAGES;
+};
+template <> struct PrefillCfg<64> {
+  static constexpr int WAVES = PREFILL_D64_WAVES, BN = PREFILL_D64_BN, STAGES = PREFILL_D64_STAGES;
+};
 
 // Chunk swizzles (16-byte chunks within a row of D bf16).
 // K is read as 16 rows x one chunk per 16 lanes: spread the 16 rows over all
@@ -56,8 +69,12 @@ __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 
-// s_waitcnt encoding (gfx9): vmcnt(0) lgkmcnt(0), expcnt unconstrained.
+// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt in
+// [6:4], lgkmcnt in [11:8].  kWaitLgkm0 | vmcnt_bits(n) waits for lgkmcnt(0)
+// and vmcnt(n) with expcnt unconstrained.
+constexpr unsigned kWaitLgkm0 = 0x0070;
 constexpr unsigned kWaitVm0Lgkm0 = 0x0070;
+constexpr unsigned vmcnt_bits(int n) { return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
 
 // One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from `gptr` land
 // at LDS byte address `lds_base` + 16 i (lds_base wave-uniform, in M0).
@@ -87,12 +104,15 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
                          float scale_log2) {
-  constexpr int BN = PrefillTile<D>::BN;
+  constexpr int BN = PrefillCfg<D>::BN;
+  constexpr int NST = PrefillCfg<D>::STAGES;
+  constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
+  constexpr int kBM = 32 * PrefillCfg<D>::WAVES;   // query rows per workgroup
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int NKB = BN / 16;               // 16-key blocks of S^T
   constexpr int NDC = D / 32;                // k-chunks of the S^T MFMA
@@ -101,12 +121,15 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int CPW = BN * CPR / kThreads;   // direct-to-LDS loads per thread per tile (K, and V)
   static_assert(CPW * kThreads == BN * CPR, "tile must split evenly");
 
-  // two stages, each K and V in its own object so that the compiler can tell
-  // the stage being read from the one being loaded
+  // the stages, each K and V in its own object so that the compiler can tell
+  // the stage being read from the ones being loaded (a third stage exists
+  // only when NST == 3)
   __shared__ __attribute__((aligned(16))) bf16 k_st0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 v_st0[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 k_st1[BN * D];
   __shared__ __attribute__((aligned(16))) bf16 v_st1[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 k_st2[NST == 3 ? BN * D : 8];
+  __shared__ __attribute__((aligned(16))) bf16 v_st2[NST == 3 ? BN * D : 8];
 
   // ---- which (q tile, batch, head) this workgroup computes ----
   const int ntq = (T + kBM - 1) / kBM;
@@ -239,11 +262,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
         mx = fmax2(mx, fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), fmax2(s[qb][kb][2], s[qb][kb][3])));
-      mx = fmax2(mx, xor_lane(mx, 16));
-      mx = fmax2(mx, xor_lane(mx, 32));
+      mx = pair_max32(pair_max16(mx));
       const float m_new = fmax2(m_run[qb], mx * scale_log2);
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_hw(m_run[qb] - m_use);
+      // the accumulator only needs rescaling when some row's maximum moved
+      const bool rescale = wave_any(m_new != m_run[qb]);
       m_run[qb] = m_new;
       float rs = 0.f;
 #pragma unroll
@@ -255,10 +279,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           rs += p;
         }
       l_part[qb] = __builtin_fmaf(l_part[qb], alpha, rs);
+      if (rescale) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+        for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha;
+          for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha;
+      }
     }
 
     // O^T += V^T P^T, 32 keys at a time; each V operand feeds both row blocks
@@ -283,29 +309,46 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
   };
 
-  // One step: wait for this tile's loads, publish it to the workgroup (which
-  // also proves every wave is done with the other stage), start loading the
-  // next tile into the other stage, compute this one.
+  // One step: wait for this tile's loads, publish the tile to the workgroup
+  // (which also proves every wave is done with the tile before, freeing its
+  // stage), start loading tile j + NST - 1 into that freed stage, compute
+  // tile j.  With three stages the load of tile j+1 may still be in flight at
+  // the wait: it was issued after tile j's, so vmcnt(2 CPW) suffices.
   auto step = [&](int j, const bf16* ks, const bf16* vs, bf16* kn, bf16* vn) {
-    __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    if (NST == 3 && j + 1 < ntk) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(2 * CPW));
+    } else {
+      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+    }
     stage_barrier();
-    if (j + 1 < ntk) load_tile(j + 1, kn, vn);
+    if (j + NST - 1 < ntk) load_tile(j + NST - 1, kn, vn);
     if (wave_live && j * BN < wave_kv_end) compute_tile(j, ks, vs);
   };
 
   load_tile(0, k_st0, v_st0);
-  for (int j = 0;;) {
-    step(j, k_st0, v_st0, k_st1, v_st1);
-    if (++j >= ntk) break;
-    step(j, k_st1, v_st1, k_st0, v_st0);
-    if (++j >= ntk) break;
+  if (NST == 3) {
+    if (1 < ntk) load_tile(1, k_st1, v_st1);
+    for (int j = 0;;) {
+      step(j, k_st0, v_st0, k_st2, v_st2);
+      if (++j >= ntk) break;
+      step(j, k_st1, v_st1, k_st0, v_st0);
+      if (++j >= ntk) break;
+      step(j, k_st2, v_st2, k_st1, v_st1);
+      if (++j >= ntk) break;
+    }
+  } else {
+    for (int j = 0;;) {
+      step(j, k_st0, v_st0, k_st1, v_st1);
+      if (++j >= ntk) break;
+      step(j, k_st1, v_st1, k_st0, v_st0);
+      if (++j >= ntk) break;
+    }
   }
 
   // ---- epilogue: O = acc / l (bf16, nearest even), LSE = ln2 * (m + log2 l) ----
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    float l_tot = l_part[qb] + xor_lane(l_part[qb], 16);
-    l_tot += xor_lane(l_tot, 32);
+    const float l_tot = pair_sum32(pair_sum16(l_part[qb]));
     const int row = wrow0 + 16 * qb + l16;
     if (row < T) {
       const float inv = 1.f / l_tot;
@@ -328,6 +371,8 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 template <int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
+  constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
+  constexpr int kBM = 32 * PrefillCfg<D>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
