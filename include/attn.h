@@ -105,25 +105,30 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   lse         [N, Hq]                          float32 log-sum-exp (written);
  *                                                       may be NULL
  *   workspace   >= attn_decode_workspace_size(N, Hq, d, max_blocks, page) bytes,
- *               16-byte aligned, device memory; scratch for the split partials,
- *               contents on entry are ignored.
+ *               16-byte aligned, device memory; scratch for the partial
+ *               results of sequences divided between workers, contents on
+ *               entry are ignored.  Two calls that share a workspace must not overlap
+ *               in time (same stream, or ordered).
  *
  * Token t of sequence n sits in page block_table[n, t / page] at slot
  * t % page.  The query attends every cached token t < seq_lens[n] (no mask
- * beyond the length).  The key range is cut into splits that are processed
- * independently and merged by their log-sum-exp; the split size only changes
- * rounding.
+ * beyond the length).  The page pairs (32 tokens) of all (sequence, KV head)
+ * segments are divided evenly over a fixed set of workers on the device; a
+ * segment divided between workers is merged by its log-sum-exp.  The
+ * division depends on seq_lens only, so equal inputs give bitwise equal
+ * results, and it only changes rounding.
  *
  * Requirements checked on the host: N, Hq, Hkv, num_pages, max_blocks >= 1;
- * Hq % Hkv == 0; scale finite and > 0; pointers aligned as for attn_fwd
- * (block_table, seq_lens 4-byte).  page must be 16, d 64 or 128, dtype
- * ATTN_BF16 and Hq / Hkv <= 16, else ATTN_EUNSUPPORTED.
+ * Hq % Hkv == 0; N * Hkv * ceil(max_blocks / 2) < 2^31; scale finite and
+ * > 0; pointers aligned as for attn_fwd (block_table, seq_lens 4-byte).
+ * page must be 16, d 64 or 128, dtype ATTN_BF16 and Hq / Hkv <= 16, else
+ * ATTN_EUNSUPPORTED.
  *
  * Device contents are a caller contract: 0 <= seq_lens[n] <= max_blocks*page
  * and block_table[n, b] in [0, num_pages) for b < ceil(seq_lens[n] / page);
- * entries past the end are never read.  The kernels never dereference a page
- * outside [0, num_pages) (such a block is skipped, and that sequence's output
- * is then unspecified), clamp lengths above max_blocks*page, and give a
+ * the values of entries past the end are never used.  The kernels never
+ * dereference a page outside [0, num_pages) (such a block is skipped, and
+ * that sequence's output is then unspecified), clamp lengths above max_blocks*page, and give a
  * sequence of length 0 the output 0 and log-sum-exp -inf.  Slots of a page at
  * or past the sequence length are never used, whatever they hold.
  */
@@ -134,7 +139,11 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int max_blocks, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid). */
+/* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid):
+ * r(N * Hq * 8) (which workers hold each sequence's pieces)
+ * + r(2 * 2048 * 16 * d * 4) (partial outputs) + r(2 * 2048 * 16 * 4) (their
+ * log-sum-exps), r() rounding up to a multiple of 256; about 34 MB at
+ * d = 128.  It does not depend on max_blocks. */
 size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page);
 
 /* Static English name of a status code. */

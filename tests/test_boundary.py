@@ -45,11 +45,22 @@ def test_status_strings():
     assert "unknown" in tea.attn_status_string(99)
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def _decode_ws(N, Hq, d):
+    """Layout documented in include/attn.h: segment waves, partials, their LSEs."""
+    waves, gmax = 2048, 16
+    return _r256(N * Hq * 8) + _r256(2 * waves * gmax * d * 4) + _r256(2 * waves * gmax * 4)
+
+
 def test_workspace_size_formula():
-    # 64 sequences, 12 heads, d=128, 512 blocks: 32 splits of 16 pages
-    o_bytes = 64 * 12 * 32 * 128 * 4
-    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == o_bytes + 64 * 12 * 32 * 4
-    assert tea.attn_decode_workspace_size(1, 1, 64, 1, 16) == 256 + 4
+    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == _decode_ws(64, 12, 128)
+    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == 33822720
+    assert tea.attn_decode_workspace_size(1, 1, 64, 1, 16) == _decode_ws(1, 1, 64)
+    # independent of max_blocks (the split is decided on the device)
+    assert tea.attn_decode_workspace_size(8, 4, 64, 7, 16) == tea.attn_decode_workspace_size(8, 4, 64, 9000, 16)
     assert tea.attn_decode_workspace_size(0, 12, 128, 512, 16) == 0
     assert tea.attn_decode_workspace_size(4, 12, 128, 512, 8) == 0
 
@@ -125,6 +136,7 @@ def _dec(**kw):
     (dict(Hq=34, Hkv=2), ATTN_EUNSUPPORTED),
     (dict(q=P + 4), ATTN_EINVAL), (dict(bt=4 * P + 2), ATTN_EINVAL),
     (dict(ws=None), ATTN_EINVAL), (dict(ws_bytes=WS - 1), ATTN_EINVAL), (dict(ws=8 * P + 8), ATTN_EINVAL),
+    (dict(N=4096, Hkv=12, Hq=12, max_blocks=1 << 17, ws_bytes=1 << 40), ATTN_EINVAL),   # > 2^31 pairs
 ])
 def test_decode_rejects_bad_arguments(bad, code):
     assert _dec(**bad) == code

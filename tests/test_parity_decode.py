@@ -141,3 +141,64 @@ def test_decode_rejects_small_workspace():
     with pytest.raises(tea.AttnError) as e:
         tea.decode_paged(q, kp, vp, bt, sl, scale=inp.scale, workspace=ws)
     assert e.value.status == tea.ATTN_EINVAL
+
+
+# Work-distribution cases: the page pairs of all sequences are divided evenly
+# over up to 2048 waves, so these exercise several 64-sequence planning
+# chunks, runs of empty sequences, totals too small for every wave (down to a
+# single wave), and one sequence cut into many pieces (more than 16, the
+# combine's load batch, and more than 64, its lane count).
+# name, N, Hq, Hkv, d, lens (0: the sequence is emptied on the device)
+def _dist_cases():
+    rng = np.random.default_rng(31)
+    many = rng.integers(0, 301, 150)
+    many[::7] = 0
+    mid = rng.integers(1, 4000, 60)
+    return [
+        ("many_seqs_chunks", 150, 8, 2, 128, many.tolist()),
+        ("tiny_total_one_wave", 3, 12, 2, 128, [1, 0, 2]),
+        ("zeros_at_ends", 70, 4, 1, 64, [0] * 5 + mid.tolist() + [0] * 5),
+        ("one_long_sequence", 1, 12, 2, 128, [8192]),
+        ("one_very_long_sequence", 1, 8, 1, 128, [65536]),
+    ]
+
+
+DIST = _dist_cases()
+
+
+@pytest.mark.parametrize("case", DIST, ids=[c[0] for c in DIST])
+def test_decode_work_distribution(case):
+    name, N, Hq, Hkv, d, lens = case
+    gen_lens = [max(1, int(x)) for x in lens]
+    inp = workloads.make_decode(N, Hq, Hkv, d, 1, max(gen_lens), seed=seed_of(name),
+                                lens=gen_lens, poison_tail=True, name=name)
+    q, kp, vp, bt, _ = _dev(inp)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    announce(f"attn_decode_paged distribution {name}: N={N} Hq={Hq} Hkv={Hkv} d={d} "
+             f"total tokens {int(sum(lens))}")
+    o, lse = tea.decode_paged(q, kp, vp, bt, sl, scale=inp.scale)
+    torch.cuda.synchronize()
+    live = [n for n in range(N) if lens[n] > 0]
+    dead = [n for n in range(N) if lens[n] == 0]
+    if dead:
+        assert torch.all(o[dead] == 0) and torch.all(torch.isneginf(lse[dead]))
+    qd, kd, vd = inp.f64()
+    o_ref, lse_ref = oracle.decode_paged(qd, kd, vd, inp.block_table, np.asarray(lens), inp.scale,
+                                         page=inp.page, seqs=live)
+    mx, mean = check_o(to_np(o[live]), o_ref, "bf16", name)
+    lmx = check_lse(to_np(lse[live]), lse_ref, name)
+    print(f"[{name}] max|dO| {mx:.3g} mean|dO| {mean:.3g} max|dLSE| {lmx:.3g}")
+
+
+def test_decode_workspace_contents_are_ignored():
+    """A workspace full of all-ones bytes (NaN floats, -1 ints) gives the same bits."""
+    inp = workloads.make_decode(16, 12, 2, 128, 512, 8192, seed=26, name="ws_poison")
+    q, kp, vp, bt, sl = _dev(inp)
+    ws = tea.decode_workspace(inp.N, inp.Hq, inp.d, inp.max_blocks, "cuda")
+    announce("attn_decode_paged with a poisoned workspace")
+    ws.zero_()
+    o0, l0 = tea.decode_paged(q, kp, vp, bt, sl, scale=inp.scale, workspace=ws)
+    ws.fill_(255)
+    o1, l1 = tea.decode_paged(q, kp, vp, bt, sl, scale=inp.scale, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o0, o1) and torch.equal(l0, l1)

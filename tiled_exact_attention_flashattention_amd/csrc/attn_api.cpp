@@ -41,27 +41,24 @@ bool overlap(const void* p, size_t n, const void* q, size_t m) {
 }
 
 constexpr int kPage = 16;
-constexpr int kMinSplitPages = 16;    // workspace is sized for the smallest split
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
 
-size_t workspace_bytes_for(int64_t N, int64_t Hq, int64_t d, int64_t max_blocks) {
-  const int64_t max_splits = (max_blocks + kMinSplitPages - 1) / kMinSplitPages;
-  const int64_t o_bytes = N * Hq * max_splits * d * 4;
-  const int64_t lse_bytes = N * Hq * max_splits * 4;
-  return (size_t)(((o_bytes + 255) / 256) * 256 + lse_bytes);
-}
+size_t round256(int64_t x) { return (size_t)((x + 255) / 256 * 256); }
 
-// Pages per split: the environment can pin it (even, 16..256, the page ids of
-// one split are staged in LDS); otherwise 32.
-int decode_split_pages() {
-  static int cached = [] {
-    const char* e = std::getenv("ATTN_DECODE_SPLIT_PAGES");
-    int v = e ? std::atoi(e) : 0;
-    if (v < kMinSplitPages || v > 256 || (v & 1)) v = 32;
-    return v;
-  }();
-  return cached;
+// Decode workspace: [segment -> (first, last) wave, N*Hq int2][partials of
+// cut segments: 2 slots per wave x 16 heads x d floats][their log-sum-exps].
+// Independent of the sequence lengths, which only the device sees.
+struct WsLayout {
+  size_t o_part, lse_part, total;
+};
+
+WsLayout decode_workspace_layout(int64_t N, int64_t Hq, int64_t d) {
+  WsLayout l;
+  l.o_part = round256(N * Hq * 8);
+  l.lse_part = l.o_part + round256((int64_t)2 * attn::kDecodeWaves * attn::kDecodeMaxG * d * 4);
+  l.total = l.lse_part + round256((int64_t)2 * attn::kDecodeWaves * attn::kDecodeMaxG * 4);
+  return l;
 }
 
 }  // namespace
@@ -82,7 +79,7 @@ const char* attn_last_error(void) { return g_last_error; }
 
 size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page) {
   if (N < 1 || Hq < 1 || d < 1 || max_blocks < 1 || page != kPage) return 0;
-  return workspace_bytes_for(N, Hq, d, max_blocks);
+  return decode_workspace_layout(N, Hq, d).total;
 }
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
@@ -150,20 +147,21 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
     return fail(ATTN_EINVAL, "attn_decode_paged: cache too large");
   if ((int64_t)N * Hq > 0x7fffffff / 1024 || N > 65535 || Hkv > 65535)
     return fail(ATTN_EINVAL, "attn_decode_paged: N, Hkv or N*Hq too large");
-  const size_t need = workspace_bytes_for(N, Hq, d, max_blocks);
-  if (!workspace || workspace_bytes < need)
-    return fail(ATTN_EINVAL, "attn_decode_paged: workspace of %zu bytes needed, %zu given", need,
-                workspace_bytes);
+  if ((int64_t)N * Hkv * ((max_blocks + 1) / 2) > 0x7fffffff)
+    return fail(ATTN_EINVAL, "attn_decode_paged: too many page pairs (N*Hkv*max_blocks/2 >= 2^31)");
+  const WsLayout lay = decode_workspace_layout(N, Hq, d);
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(ATTN_EINVAL, "attn_decode_paged: workspace of %zu bytes needed, %zu given",
+                lay.total, workspace_bytes);
   if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "attn_decode_paged: misaligned workspace");
 
-  const int max_splits = (max_blocks + kMinSplitPages - 1) / kMinSplitPages;
-  float* o_part = static_cast<float*>(workspace);
-  const size_t o_bytes = (size_t)N * Hq * max_splits * d * 4;
-  float* lse_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + ((o_bytes + 255) / 256) * 256);
-  const int split_pages = decode_split_pages();
-  hipError_t e = attn::launch_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, o_part,
-                                           lse_part, N, Hq, Hkv, d, num_pages, max_blocks,
-                                           split_pages, max_splits, scale * kLog2e,
+  char* ws = static_cast<char*>(workspace);
+  attn::DecodeWorkspace dw;
+  dw.seg_waves = reinterpret_cast<int2*>(ws);
+  dw.o_part = reinterpret_cast<float*>(ws + lay.o_part);
+  dw.lse_part = reinterpret_cast<float*>(ws + lay.lse_part);
+  hipError_t e = attn::launch_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, dw,
+                                           N, Hq, Hkv, d, num_pages, max_blocks, scale * kLog2e,
                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_EHIP, "attn_decode_paged: %s", hipGetErrorString(e));
   return ATTN_OK;

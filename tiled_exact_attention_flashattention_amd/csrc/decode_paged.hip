@@ -7,25 +7,38 @@
 // attention; 16-token pages as in its serving example).  The attention itself
 // is the same online-softmax recurrence as the prefill kernel ("Advanced
 // Attention Mechanisms - II", sections "Softmax stabiliser" and "Incremental /
-// online softmax").
+// online softmax"); pieces of one sequence that are computed apart are merged
+// by their log-sum-exp, LSE = M + ln sum_j exp(lse_j - M),
+// O = sum_j exp(lse_j - LSE) O_j, the same rescaling the online softmax uses.
 //
-// A single query row cannot fill the machine, so the key range of each
-// sequence is cut into splits of `split_pages` pages:
-//   decode_split_kernel:  one workgroup per (split, KV head, sequence).  All
-//     Hq/Hkv query heads that share the KV head are served from one read of
-//     each K/V page (the query heads are the 16 columns of a 16x16x32 MFMA).
-//     The 4 waves take page pairs round-robin, each with its own running
-//     (m, l, acc); the waves are merged through LDS and the split writes its
-//     normalised partial output and log-sum-exp to the workspace.
-//   decode_combine_kernel: per (sequence, head) merges the splits by their
-//     log-sum-exp: LSE = M + ln sum_s exp(lse_s - M), O = sum_s exp(lse_s - LSE) O_s.
-// The combine is exact algebra of the same rescaling the online softmax uses.
+// Work distribution.  The unit of work is a page pair (32 keys) of one
+// (sequence, KV head) segment; units are numbered sequence-major, then KV
+// head, then pair.  A persistent grid of kDecodeWaves single-wave workgroups
+// (8 per CU on 256 CUs) splits the U units into equal contiguous ranges, so
+// every CU carries the same load: the kernel is bound by HBM and a CU's share
+// of the bandwidth grows with the waves it holds, so an uneven spread of
+// waves over CUs, not the bytes in flight, is what a fixed split size loses.
+//   decode_stream_kernel: each wave finds its range from seq_lens (prefix
+//     sums over 64 sequences at a time) and walks it.  A segment that lies
+//     wholly inside the range is finished in place; a segment cut by a range
+//     boundary leaves a normalised partial and its log-sum-exp in one of the
+//     wave's two slots, and the wave holding the segment's first pair records
+//     which waves hold its pieces.
+//   decode_combine_kernel: one wave per (sequence, query head) merges the
+//     pieces of cut segments and writes the output of empty sequences.  The
+//     kernel boundary orders the partials' writes before their reads, which
+//     a merge inside the first kernel would need device-wide fences for (on
+//     this chip those write back and invalidate every XCD's L2).
 //
-// Memory: K of a page is read straight into MFMA A-operand registers (each
-// lane one key row, 16 bytes per d-chunk); V of a page pair is copied
-// row-major into the wave's LDS slice and read back transposed with the
-// gfx950 LDS transpose read.  Positions at or past the sequence length, and
-// pages outside [0, num_pages), are masked and never dereferenced.
+// Inside a wave, page pairs (K and V, 16 KB at d = 128) are staged through a
+// two-deep queue of registers: while one pair is consumed the next two are
+// on their way, and the page ids of the pair after those travel with them.
+// K of a pair is used straight from registers as MFMA A operands (each lane
+// one key row, 16 bytes per d-chunk); V is copied row-major into the wave's
+// LDS slice and read back transposed with the gfx950 LDS transpose read.
+// All Hq/Hkv query heads of a KV head are the 16 columns of a 16x16x32 MFMA.
+// Positions at or past the sequence length, and pages outside
+// [0, num_pages), are masked and never dereferenced.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
@@ -33,11 +46,25 @@ namespace attn {
 namespace {
 
 constexpr int kPage = 16;
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-constexpr int kMaxSplitPages = 256;   // page ids of one split staged in LDS
+constexpr int kMinPairsPerWave = 4;   // fewer units than 4 per wave: use fewer waves
 
-// 16-byte-chunk swizzle of V row `row` in a wave's LDS slice.  The transpose
+__device__ __forceinline__ int wave_sum(int x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    const int y = __shfl_up(x, m);
+    if (lane >= m) x += y;
+  }
+  return x;
+}
+
+// 16-byte-chunk swizzle of V row `row` in the wave's LDS slice.  The transpose
 // read takes 8 consecutive rows x 32 bytes per half-wave; XOR-ing the chunk
 // pair index spreads those rows over distinct bank groups.  Rows r and r+16
 // (the same slot of the two pages of a pair) share the swizzle.
@@ -46,132 +73,262 @@ __device__ __forceinline__ int dv_swz(int row) {
   return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
 }
 
+__device__ __forceinline__ int clamp_len(int len, int max_blocks) {
+  return max(0, min(len, max_blocks * kPage));
+}
+
+// ---------------------------------------------------------------------------
+// Stream kernel.
+
+// Registers of one page pair in flight: K as A operands, V as row chunks.
 template <int D>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kpool,
-                         const bf16* __restrict__ vpool, const int32_t* __restrict__ block_table,
-                         const int32_t* __restrict__ seq_lens, float* __restrict__ o_part,
-                         float* __restrict__ lse_part, int Hq, int Hkv, int num_pages,
-                         int max_blocks, int split_pages, int max_splits, float scale_log2) {
-  constexpr int WAVE_LDS = 2 * kPage * D;     // one page pair, [32 rows][D], swizzled
-  constexpr int NDC = D / 32;                 // k-chunks of the S^T MFMA
+struct PairRegs {
+  static constexpr int NDC = D / 32;                    // k-chunks of the S^T MFMA
+  static constexpr int VCH = 2 * kPage * (D / 8) / 64;  // V chunks per lane
+  bf16x8 k[2][NDC];
+  u32x4 v[VCH];
+};
+
+// One page pair, all fields wave-uniform.  n < 0 marks a padding pair.
+struct PairMeta {
+  int n, hk, p, np, len, u;   // sequence, KV head, pair in segment, pairs in segment, tokens, unit
+  int tv0, tv1;               // tokens of page 0 / page 1 that take part (0: masked)
+};
+
+template <int D>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
+void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kpool,
+                          const bf16* __restrict__ vpool, const int32_t* __restrict__ block_table,
+                          const int32_t* __restrict__ seq_lens, bf16* __restrict__ o,
+                          float* __restrict__ lse, int2* __restrict__ seg_waves,
+                          float* __restrict__ o_part, float* __restrict__ lse_part, int N, int Hq,
+                          int Hkv, int num_pages, int max_blocks, float scale_log2) {
+  constexpr int NDC = PairRegs<D>::NDC;
+  constexpr int VCH = PairRegs<D>::VCH;
   constexpr int NDB = D / 16;                 // 16-row blocks of O^T
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int VCH = 2 * kPage * CPR / 64;   // V chunks per lane per pair
-  constexpr int RED_STRIDE = D + 4;           // fp32 row stride of the merge buffer
 
-  // LDS: [4 wave slices of V][page ids of this split]; the merge buffer of
-  // the epilogue reuses the V slices.
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  int32_t* pages = reinterpret_cast<int32_t*>(smem + kWaves * WAVE_LDS);
+  __shared__ __attribute__((aligned(16))) bf16 vl[2 * kPage * D];   // one V pair, swizzled
 
-  const int split = blockIdx.x, hk = blockIdx.y, n = blockIdx.z;
-  int len = seq_lens[n];
-  len = max(0, min(len, max_blocks * kPage));
-  const int blk0 = split * split_pages;
-  if (blk0 * kPage >= len) return;            // whole workgroup: nothing in this split
-  const int nblk = (len + kPage - 1) / kPage;
-  const int blk_end = min(blk0 + split_pages, nblk);
-  const int nb = blk_end - blk0;              // blocks of this split
-  const int npairs = (nb + 1) >> 1;
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x;
+  auto pairs_of = [&](int n) {
+    return n < N ? (clamp_len(seq_lens[n], max_blocks) + 2 * kPage - 1) / (2 * kPage) : 0;
+  };
+
+  // ---- this wave's unit range [a, b) and where it starts ----
+  // (readfirstlane: the cross-lane sums are equal in every lane; saying so
+  // keeps the whole walk in scalar registers and scalar branches)
+  int pairs = 0;                              // page pairs of all sequences (< 2^31 / Hkv)
+  for (int c0 = 0; c0 < N; c0 += 64)
+    pairs += __builtin_amdgcn_readfirstlane(wave_sum(pairs_of(c0 + lane)));
+  const int U = pairs * Hkv;
+  const int W = U == 0 ? 0 : min(kDecodeWaves, max(1, U / kMinPairsPerWave));
+  if (w >= W) return;
+  const int a = (int)((long long)w * U / W), b = (int)((long long)(w + 1) * U / W);
+  const int L = b - a;                        // >= 1 units
+  int st_n = 0, st_np = 0, st_pairs_before = 0;
+  for (int c0 = 0, base = 0;; c0 += 64) {     // sequence n whose units contain unit a
+    const int np = pairs_of(c0 + lane);
+    const int incl = wave_incl_scan(np);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64((base + incl) * Hkv > a);
+    if (hit != 0) {
+      const int j = __builtin_ctzll(hit);
+      st_n = c0 + j;
+      st_np = __builtin_amdgcn_readlane(np, j);
+      st_pairs_before = base + __builtin_amdgcn_readlane(incl, j) - st_np;
+      break;
+    }
+    base += __builtin_amdgcn_readlane(incl, 63);
+  }
+  const int st_off = a - st_pairs_before * Hkv;
+  const int4 st = make_int4(st_n, st_off / st_np, st_off % st_np, 0);
 
   const int G = Hq / Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
+  const size_t page_stride = (size_t)Hkv * kPage * D;     // elements per page
 
-  // page ids of the whole split, once (-1 marks a block outside [0, num_pages))
-  for (int i = tid; i < nb; i += kThreads) {
-    const int p = block_table[(size_t)n * max_blocks + blk0 + i];
-    pages[i] = (p >= 0 && p < num_pages) ? p : -1;
-  }
+  // wave holding unit u
+  auto wave_of = [&](int u) { return (int)(((long long)(u + 1) * W - 1) / U); };
 
-  // Q operand (B of S^T = K Q^T): column l16 = query head hk*G + l16.
+  // ---- cursor over this wave's units (wave-uniform) ----
+  int c_k = 0, c_n = st.x, c_hk = st.y, c_p = st.z;
+  int c_len = clamp_len(seq_lens[c_n], max_blocks);
+  int c_np = (c_len + 2 * kPage - 1) / (2 * kPage);
+  auto cur_meta = [&]() {
+    PairMeta m;
+    if (c_k < L) {
+      m.n = c_n; m.hk = c_hk; m.p = c_p; m.np = c_np; m.len = c_len; m.u = a + c_k;
+    } else {
+      m.n = -1; m.hk = 0; m.p = 0; m.np = 1; m.len = 0; m.u = -1;
+    }
+    m.tv0 = m.tv1 = 0;
+    return m;
+  };
+  auto advance = [&]() {
+    if (++c_k >= L) return;
+    if (++c_p < c_np) return;
+    c_p = 0;
+    if (++c_hk < Hkv) return;
+    c_hk = 0;
+    do {                                      // a later unit exists, so this ends before N
+      ++c_n;
+      c_len = clamp_len(seq_lens[c_n], max_blocks);
+      c_np = (c_len + 2 * kPage - 1) / (2 * kPage);
+    } while (c_np == 0);
+  };
+  // Page ids of the cursor's pair: lane 0 block 2p, lane 1 block 2p+1 (both
+  // clamped to the last block), other lanes repeat them.  Padding reads entry 0.
+  auto load_pid = [&]() {
+    size_t idx = 0;
+    if (c_k < L) {
+      const int nblk = (c_len + kPage - 1) / kPage;
+      idx = (size_t)c_n * max_blocks + min(2 * c_p + (lane & 1), nblk - 1);
+    }
+    return block_table[idx];
+  };
+
+  // ---- Q operand (B of S^T = K Q^T): column l16 = query head hk*G + l16 ----
   bf16x8 qop[NDC];
-  if (l16 < G) {
-    const bf16* qp = q + ((size_t)n * Hq + hk * G + l16) * D + 8 * g;
+  int q_n = -1, q_hk = -1;
+  auto load_q = [&](int n, int hk) {
+    const bf16* qp = q + ((size_t)n * Hq + hk * G + min(l16, G - 1)) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < NDC; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qp + 32 * c);
-  } else {
+    if (l16 >= G) {
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) qop[c] = bf16x8{};
-  }
-  __syncthreads();
+      for (int c = 0; c < NDC; ++c) qop[c] = bf16x8{};
+    }
+    q_n = n;
+    q_hk = hk;
+  };
 
   float m_run = -INFINITY, l_part = 0.f;
   f32x4 acc[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
 
-  bf16* vl = smem + wave * WAVE_LDS;
-  const size_t page_stride = (size_t)Hkv * kPage * D;     // elements per page
-  const size_t head_off = (size_t)hk * kPage * D;
-
-  // transpose-read address of this lane inside a slice (page 0; +16 rows for page 1)
+  // transpose-read address of this lane inside the slice (page 0; +16 rows for page 1)
   const int vrow = 4 * g + (l16 >> 2);
   const int vsw = dv_swz<D>(vrow);
   const bf16* vrd = vl + vrow * D + 4 * (l16 & 1);
   const int vchunk = (l16 & 3) >> 1;
 
-  // Loads of one page pair into registers: K as MFMA A-operands (lane key
-  // l16, d = 32c + 8g..+7), V as coalesced 16-byte row chunks.  The loads are
-  // unconditional so that each page needs one base address: a block without a
-  // valid page reads page 0 instead (in bounds), and its scores are masked and
-  // its V rows zeroed before use, like the slots at or past the length.
-  auto page_of = [&](int blk) { return blk < nb ? max(pages[blk], 0) : 0; };
-  auto issue_k = [&](int pi, bf16x8 (&kop)[2][NDC]) {
+  // K/V loads of pair m (page ids in pid): unconditional, so that the number
+  // of loads in flight is the same on every path and the compiler's wait
+  // counts stay exact.  A masked page (and a padding pair) reads page 0 of
+  // KV head 0, which is in bounds and stays in L2.
+  auto issue = [&](PairRegs<D>& r, int pid, PairMeta& m) {
+    const int id0 = __builtin_amdgcn_readlane(pid, 0), id1 = __builtin_amdgcn_readlane(pid, 1);
+    const bool ok0 = m.n >= 0 && id0 >= 0 && id0 < num_pages;
+    const bool ok1 = m.n >= 0 && id1 >= 0 && id1 < num_pages;
+    const int t0 = m.len - 2 * kPage * m.p;
+    m.tv0 = ok0 ? max(0, min(t0, kPage)) : 0;
+    m.tv1 = ok1 ? max(0, min(t0 - kPage, kPage)) : 0;
+    const size_t head_off = (size_t)(m.n >= 0 ? m.hk : 0) * kPage * D;
+    const size_t off0 = (ok0 ? (size_t)id0 * page_stride : 0) + head_off;
+    const size_t off1 = (ok1 ? (size_t)id1 * page_stride : 0) + head_off;
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bf16* kp = kpool + (size_t)page_of(2 * pi + p) * page_stride + head_off + l16 * D + 8 * g;
+      const bf16* kp = kpool + (p ? off1 : off0) + l16 * D + 8 * g;
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) kop[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
+      for (int c = 0; c < NDC; ++c) r.k[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
     }
-  };
-  auto issue_v = [&](int pi, u32x4 (&vreg)[VCH]) {
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bf16* vp = vpool + (size_t)page_of(2 * pi + p) * page_stride + head_off + lane * 8;
+      const bf16* vp = vpool + (p ? off1 : off0) + lane * 8;
 #pragma unroll
-      for (int r = 0; r < VCH / 2; ++r) vreg[p * (VCH / 2) + r] = load16(vp + 64 * 8 * r);
-    }
-  };
-  auto block_ok = [&](int blk) { return blk < nb && pages[blk] >= 0; };
-  // V chunk r of page p is row (lane + 64 r) / CPR of that page
-  auto write_v = [&](int pi, const u32x4 (&vreg)[VCH]) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const bool ok = block_ok(2 * pi + p);
-#pragma unroll
-      for (int r = 0; r < VCH / 2; ++r) {
-        const int c = lane + 64 * r;
-        const int slot = c / CPR, col = c % CPR;
-        const int row = 16 * p + slot;
-        const bool live = ok && (blk0 + 2 * pi + p) * kPage + slot < len;
-        const u32x4 zero = {0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(vl + row * D + (col ^ dv_swz<D>(row)) * 8) =
-            live ? vreg[p * (VCH / 2) + r] : zero;
-      }
+      for (int c = 0; c < VCH / 2; ++c) r.v[p * (VCH / 2) + c] = load16(vp + 64 * 8 * c);
     }
   };
 
-  auto compute = [&](int pi, const bf16x8 (&kop)[2][NDC]) {
-    const int bl = 2 * pi;
+  // Writes the result of the piece that ends with pair m and resets the state.
+  auto finish_piece = [&](const PairMeta& m) {
+    const float l_tot = pair_sum32(pair_sum16(l_part));
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+    const int s = m.u - m.p, e = s + m.np;
+    if (s >= a && lane == 0)                  // this wave holds the segment's first pair
+      seg_waves[(size_t)m.n * Hkv + m.hk] = make_int2(w, wave_of(e - 1));
+    if (s >= a && e <= b) {                   // whole segment in this wave: final output
+      if (l16 < G) {
+        const size_t row = (size_t)m.n * Hq + m.hk * G + l16;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          bf16x4 x;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[i] = (bf16)(acc[db][i] * inv);
+          *reinterpret_cast<bf16x4*>(o + row * D + 16 * db + 4 * g) = x;
+        }
+        if (g == 0 && lse != nullptr) lse[row] = lse_v;
+      }
+    } else {                                  // cut segment: partial into slot (w, kind)
+      const int kind = s < a ? 0 : 1;         // 1: the segment's first piece
+      const size_t slot = 2 * (size_t)w + kind;
+      if (l16 < G) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          *reinterpret_cast<f32x4*>(o_part + (slot * kDecodeMaxG + l16) * D + 16 * db + 4 * g) =
+              acc[db] * inv;
+        if (g == 0) lse_part[slot * kDecodeMaxG + l16] = lse_v;
+      }
+    }
+    m_run = -INFINITY;
+    l_part = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc[db] = f32x4{};
+  };
+
+  // One pair: V to LDS, S^T = K Q^T, the online-softmax update, then
+  // O^T += V^T P^T.  As soon as S has consumed K, r takes the loads of pair
+  // `mp` (page ids in pid), and pid takes the ids of the pair after that.
+  auto step = [&](PairRegs<D>& r, PairMeta& mk, int& pid, PairMeta& mp) {
+    const PairMeta m = mk;
+    // V chunk c of page p is row (lane + 64 c) / CPR of that page
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int tv = p ? m.tv1 : m.tv0;
+#pragma unroll
+      for (int c = 0; c < VCH / 2; ++c) {
+        const int ch = lane + 64 * c;
+        const int slot = ch / CPR, col = ch % CPR;
+        const int row = 16 * p + slot;
+        const u32x4 zero = {0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(vl + row * D + (col ^ dv_swz<D>(row)) * 8) =
+            slot < tv ? r.v[p * (VCH / 2) + c] : zero;
+      }
+    }
+    // A new segment needs its query rows.  The wait for them is taken inside
+    // the branch (the empty asm consumes the registers), so the loop's other
+    // paths keep their wait counts.
+    if (m.n >= 0 && (m.n != q_n || m.hk != q_hk)) {
+      load_q(m.n, m.hk);
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(qop[c]));
+    }
     // S^T[key][head] for both pages
     f32x4 s[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
       s[p] = f32x4{};
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) s[p] = mfma_16x16x32(kop[p][c], qop[c], s[p]);
+      for (int c = 0; c < NDC; ++c) s[p] = mfma_16x16x32(r.k[p][c], qop[c], s[p]);
     }
-    // mask positions past the length and blocks without a valid page
+    __builtin_amdgcn_sched_barrier(0);
+    issue(r, pid, mp);
+    mk = mp;
+    mp = cur_meta();
+    pid = load_pid();
+    advance();
+    __builtin_amdgcn_sched_barrier(0);
+
+    // mask positions past the length and masked pages
 #pragma unroll
     for (int p = 0; p < 2; ++p) {
-      const bool ok = block_ok(bl + p);
+      const int tv = p ? m.tv1 : m.tv0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = (blk0 + bl + p) * kPage + 4 * g + i;
-        if (!ok || tok >= len) s[p][i] = -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i)
+        if (4 * g + i >= tv) s[p][i] = -INFINITY;
     }
 
     float mx = fmax2(fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3])),
@@ -221,107 +378,92 @@ void decode_split_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kp
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    if (m.n >= 0 && (m.p == m.np - 1 || m.u == b - 1)) finish_piece(m);
   };
 
-  // Software pipeline: K has two register sets, V one (it moves to LDS at the
-  // top of each step, after which its registers take the next pair's V).
-  // The loads of pair pi + 4 are in flight while pair pi is computed.  Every
-  // load is issued unconditionally -- past the last pair the index is clamped,
-  // re-reading that pair from L2 -- so the number of loads in flight is the
-  // same on every path and the compiler's wait counts stay exact; a load
-  // behind a branch would make it wait for the prefetched pair as well.
-  bf16x8 ka[2][NDC], kb[2][NDC];
-  u32x4 vreg[VCH];
-  if (wave < npairs) {
-    auto clampp = [&](int pi) { return min(pi, npairs - 1); };
-    issue_k(wave, ka);
-    issue_v(wave, vreg);
-    for (int pi = wave;; pi += 2 * kWaves) {
-      write_v(pi, vreg);
-      issue_k(clampp(pi + kWaves), kb);
-      issue_v(clampp(pi + kWaves), vreg);
-      compute(pi, ka);
-      if (pi + kWaves >= npairs) break;
-      write_v(pi + kWaves, vreg);
-      issue_k(clampp(pi + 2 * kWaves), ka);
-      issue_v(clampp(pi + 2 * kWaves), vreg);
-      compute(pi + kWaves, kb);
-      if (pi + 2 * kWaves >= npairs) break;
-    }
-  }
+  // ---- prologue: page ids of pairs 0 and 1, their K/V, then the ids of 2 and 3 ----
+  load_q(st.x, st.y);
+  PairMeta ma = cur_meta();
+  int pida = load_pid();
+  advance();
+  PairMeta mb = cur_meta();
+  int pidb = load_pid();
+  advance();
+  PairRegs<D> ra, rb;
+  __builtin_amdgcn_sched_barrier(0);
+  issue(ra, pida, ma);
+  PairMeta mpa = cur_meta();
+  pida = load_pid();
+  advance();
+  __builtin_amdgcn_sched_barrier(0);      // keep set a's loads ahead of set b's
+  issue(rb, pidb, mb);
+  PairMeta mpb = cur_meta();
+  pidb = load_pid();
+  advance();
+  __builtin_amdgcn_sched_barrier(0);
 
-  // ---- merge the 4 waves of this split through LDS ----
-  const float l_tot = pair_sum32(pair_sum16(l_part));
-  __syncthreads();                                   // all V slices consumed
-  float* red_o = reinterpret_cast<float*>(smem);     // [wave][16 heads][RED_STRIDE]
-  float* red_m = red_o + kWaves * 16 * RED_STRIDE;   // [wave][16]
-  float* red_l = red_m + kWaves * 16;                // [wave][16]
-#pragma unroll
-  for (int db = 0; db < NDB; ++db)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      red_o[(wave * 16 + l16) * RED_STRIDE + 16 * db + 4 * g + i] = acc[db][i];
-  if (g == 0) {
-    red_m[wave * 16 + l16] = m_run;
-    red_l[wave * 16 + l16] = l_tot;
-  }
-  __syncthreads();
-
-  // thread -> (head, d-slice): 16 threads per head, D/16 values each
-  const int hh = tid >> 4, part = tid & 15;
-  if (hh < G) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmax2(M, red_m[w * 16 + hh]);
-    float wgt[kWaves];
-    float L = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      wgt[w] = (M == -INFINITY) ? 0.f : exp2f(red_m[w * 16 + hh] - M);
-      L = __builtin_fmaf(red_l[w * 16 + hh], wgt[w], L);
-    }
-    const float inv = L > 0.f ? 1.f / L : 0.f;
-    const int head = hk * G + hh;
-    const size_t slot = ((size_t)n * Hq + head) * max_splits + split;
-    float* op = o_part + slot * D;
-#pragma unroll
-    for (int e = 0; e < D / 16; ++e) {
-      const int d = part * (D / 16) + e;
-      float x = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) x = __builtin_fmaf(red_o[(w * 16 + hh) * RED_STRIDE + d], wgt[w], x);
-      op[d] = x * inv;
-    }
-    if (part == 0) lse_part[slot] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
-  }
+  // Two register sets alternate and the loop always runs both steps (an odd
+  // count gets one padding pair), so the loop has a single exit: with an exit
+  // between the steps the compiler's wait counts would have to allow for
+  // either order of the two sets and wait for both.
+  int k = 0;                                  // L >= 1: no loop guard
+  do {
+    step(ra, ma, pida, mpa);
+    step(rb, mb, pidb, mpb);
+    k += 2;
+  } while (k < L);
 }
 
-// One wave per (sequence, head): lane s holds split s's log-sum-exp (splits
-// beyond 64 are folded in a loop), the wave reduces max and sum, then each
-// lane accumulates D/64 output elements over the splits.
+// One wave per (sequence, query head).  An empty sequence gets O = 0 and
+// LSE = -inf; a segment finished by one wave is left alone; a cut segment's
+// pieces (slot 2*w_first + 1, then slot 2*w for each later wave) are merged
+// by their log-sum-exp.  Lane j keeps piece j's log-sum-exp (more than 64
+// pieces are folded in a loop); each lane accumulates D/64 output elements,
+// sixteen pieces' loads at a time.
 template <int D>
 __global__ __launch_bounds__(64)
-void decode_combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                           const int32_t* __restrict__ seq_lens, bf16* __restrict__ o,
-                           float* __restrict__ lse, int Hq, int max_blocks, int split_pages,
-                           int max_splits) {
+void decode_combine_kernel(const int32_t* __restrict__ seq_lens, const int2* __restrict__ seg_waves,
+                           const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                           bf16* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv,
+                           int max_blocks) {
   constexpr int PER = D / 64;
+  constexpr int CH = 16;
   const int nh = blockIdx.x;
-  const int n = nh / Hq;
+  const int n = nh / Hq, h = nh - n * Hq;
+  const int G = Hq / Hkv, hk = h / G, hh = h - hk * G;
   const int lane = threadIdx.x;
-  int len = seq_lens[n];
-  len = max(0, min(len, max_blocks * kPage));
-  const int nsplit = (len + split_pages * kPage - 1) / (split_pages * kPage);
-  const float* lp = lse_part + (size_t)nh * max_splits;
-  const float* op = o_part + (size_t)nh * max_splits * D;
+  bf16* orow = o + (size_t)nh * D + lane * PER;
+  if (clamp_len(seq_lens[n], max_blocks) == 0) {
+#pragma unroll
+    for (int e = 0; e < PER; ++e) orow[e] = (bf16)0.f;
+    if (lse != nullptr && lane == 0) lse[nh] = -INFINITY;
+    return;
+  }
+  const int2 ws = seg_waves[(size_t)n * Hkv + hk];
+  if (ws.x == ws.y) return;                   // finished in place
+  if (ws.x < 0 || ws.y < ws.x || ws.y >= kDecodeWaves) return;   // never written: not ours
+  const int npieces = ws.y - ws.x + 1;
+  auto slot_of = [&](int j) { return (size_t)(2 * (ws.x + j) + (j == 0 ? 1 : 0)) * kDecodeMaxG + hh; };
 
-  float M = -INFINITY;
-  for (int s = lane; s < nsplit; s += 64) M = fmax2(M, lp[s]);
+  // loads of the first chunk of pieces (indices clamped to the last piece)
+  float x[CH][PER];
+#pragma unroll
+  for (int u = 0; u < CH; ++u) {
+    const float* op = o_part + slot_of(min(u, npieces - 1)) * D + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) x[u][e] = op[e];
+  }
+  const float own = lane < npieces ? lse_part[slot_of(lane)] : -INFINITY;
+  float M = own;
+  for (int j = lane + 64; j < npieces; j += 64) M = fmax2(M, lse_part[slot_of(j)]);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmax2(M, xor_lane(M, m));
   float W = 0.f;
-  if (M != -INFINITY)
-    for (int s = lane; s < nsplit; s += 64) W += expf(lp[s] - M);
+  if (M != -INFINITY) {
+    W = lane < npieces ? expf(own - M) : 0.f;
+    for (int j = lane + 64; j < npieces; j += 64) W += expf(lse_part[slot_of(j)] - M);
+  }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) W += xor_lane(W, m);
 
@@ -329,51 +471,45 @@ void decode_combine_kernel(const float* __restrict__ o_part, const float* __rest
 #pragma unroll
   for (int e = 0; e < PER; ++e) out[e] = 0.f;
   if (W > 0.f) {
-    int s = 0;
-    for (; s + 4 <= nsplit; s += 4) {
-      float w[4], x[4][PER];
+    for (int j0 = 0;; j0 += CH) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        w[u] = expf(lp[s + u] - M);
+      for (int u = 0; u < CH; ++u) {
+        const int j = j0 + u;
+        const float lj = j < 64 ? __shfl(own, j & 63) : lse_part[slot_of(min(j, npieces - 1))];
+        const float wj = j < npieces ? expf(lj - M) : 0.f;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) x[u][e] = op[(size_t)(s + u) * D + lane * PER + e];
+        for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(wj, x[u][e], out[e]);
       }
+      if (j0 + CH >= npieces) break;
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < CH; ++u) {
+        const float* op = o_part + slot_of(min(j0 + CH + u, npieces - 1)) * D + lane * PER;
 #pragma unroll
-        for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(w[u], x[u][e], out[e]);
-    }
-    for (; s < nsplit; ++s) {
-      const float w = expf(lp[s] - M);
-#pragma unroll
-      for (int e = 0; e < PER; ++e) out[e] = __builtin_fmaf(w, op[(size_t)s * D + lane * PER + e], out[e]);
+        for (int e = 0; e < PER; ++e) x[u][e] = op[e];
+      }
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) o[(size_t)nh * D + lane * PER + e] = (bf16)(out[e] * inv);
+  for (int e = 0; e < PER; ++e) orow[e] = (bf16)(out[e] * inv);
   if (lse != nullptr && lane == 0) lse[nh] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
 template <int D>
 hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
-                    float* o_part, float* lse_part, int N, int Hq, int Hkv, int num_pages,
-                    int max_blocks, int split_pages, int max_splits, float scale_log2,
-                    hipStream_t stream) {
-  constexpr size_t v_lds = (size_t)kWaves * 2 * kPage * D * sizeof(bf16) + kMaxSplitPages * 4;
-  constexpr size_t red_lds = ((size_t)kWaves * 16 * (D + 4) + 2 * kWaves * 16) * sizeof(float);
-  constexpr size_t smem = v_lds > red_lds ? v_lds : red_lds;
-  const int nsplit_grid = (max_blocks + split_pages - 1) / split_pages;
-  hipLaunchKernelGGL((decode_split_kernel<D>), dim3(nsplit_grid, Hkv, N), dim3(kThreads), smem,
-                     stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k_pool),
-                     static_cast<const bf16*>(v_pool), block_table, seq_lens, o_part, lse_part, Hq,
-                     Hkv, num_pages, max_blocks, split_pages, max_splits, scale_log2);
+                    const DecodeWorkspace& ws, int N, int Hq, int Hkv, int num_pages,
+                    int max_blocks, float scale_log2, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<D>), dim3(kDecodeWaves), dim3(64), 0, stream,
+                     static_cast<const bf16*>(q), static_cast<const bf16*>(k_pool),
+                     static_cast<const bf16*>(v_pool), block_table, seq_lens,
+                     static_cast<bf16*>(o), lse, ws.seg_waves, ws.o_part, ws.lse_part, N, Hq, Hkv,
+                     num_pages, max_blocks, scale_log2);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(N * Hq), dim3(64), 0, stream, o_part,
-                     lse_part, seq_lens, static_cast<bf16*>(o), lse, Hq, max_blocks, split_pages,
-                     max_splits);
+  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(N * Hq), dim3(64), 0, stream, seq_lens,
+                     ws.seg_waves, ws.o_part, ws.lse_part, static_cast<bf16*>(o), lse, Hq, Hkv,
+                     max_blocks);
   return hipGetLastError();
 }
 
@@ -381,14 +517,14 @@ hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
 
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* seq_lens, void* o,
-                               float* lse, float* o_part, float* lse_part, int N, int Hq, int Hkv,
-                               int d, int num_pages, int max_blocks, int split_pages,
-                               int max_splits, float scale_log2, hipStream_t stream) {
+                               float* lse, const DecodeWorkspace& ws, int N, int Hq, int Hkv,
+                               int d, int num_pages, int max_blocks, float scale_log2,
+                               hipStream_t stream) {
   if (d == 128)
-    return launch_d<128>(q, k_pool, v_pool, block_table, seq_lens, o, lse, o_part, lse_part, N, Hq,
-                         Hkv, num_pages, max_blocks, split_pages, max_splits, scale_log2, stream);
-  return launch_d<64>(q, k_pool, v_pool, block_table, seq_lens, o, lse, o_part, lse_part, N, Hq,
-                      Hkv, num_pages, max_blocks, split_pages, max_splits, scale_log2, stream);
+    return launch_d<128>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N, Hq, Hkv,
+                         num_pages, max_blocks, scale_log2, stream);
+  return launch_d<64>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N, Hq, Hkv, num_pages,
+                      max_blocks, scale_log2, stream);
 }
 
 }  // namespace attn

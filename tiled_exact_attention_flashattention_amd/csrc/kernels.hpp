@@ -19,14 +19,22 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
                               int B, int Hq, int Hkv, int T, int S, int d,
                               float scale_log2, bool causal, hipStream_t stream);
 
-// Paged decode: split kernel + log-sum-exp combine, back to back on `stream`.
-// o_part/lse_part live in the caller's workspace with `max_splits` splits per
-// (sequence, head); split_pages pages per split (even, >= 16).
+// Paged decode: a persistent grid of kDecodeWaves single-wave workgroups that
+// split all page pairs evenly, then a combine kernel for the sequences they
+// cut.  Workspace pieces, all 16-byte aligned, laid out by the C ABI layer:
+constexpr int kDecodeWaves = 2048;   // 8 per CU on 256 CUs
+constexpr int kDecodeMaxG = 16;      // query heads per KV head, slot stride
+
+struct DecodeWorkspace {
+  int2* seg_waves;                   // [N * Hkv] first and last wave of each segment
+  float* o_part;                     // [2 * kDecodeWaves][kDecodeMaxG][d] cut-segment partials
+  float* lse_part;                   // [2 * kDecodeWaves][kDecodeMaxG]
+};
+
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* seq_lens,
-                               void* o, float* lse, float* o_part, float* lse_part,
+                               void* o, float* lse, const DecodeWorkspace& ws,
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
-                               int split_pages, int max_splits, float scale_log2,
-                               hipStream_t stream);
+                               float scale_log2, hipStream_t stream);
 
 }  // namespace attn
