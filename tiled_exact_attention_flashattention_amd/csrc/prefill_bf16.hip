@@ -69,6 +69,10 @@ __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 
+// Slack of the running maximum (log2 units): P = exp2(s - m) may reach
+// 2^kLazyTau, far inside bf16 and fp32 range.
+constexpr float kLazyTau = 8.f;
+
 // s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt in
 // [6:4], lgkmcnt in [11:8].  kWaitLgkm0 | vmcnt_bits(n) waits for lgkmcnt(0)
 // and vmcnt(n) with expcnt unconstrained.
@@ -76,17 +80,18 @@ constexpr unsigned kWaitLgkm0 = 0x0070;
 constexpr unsigned kWaitVm0Lgkm0 = 0x0070;
 constexpr unsigned vmcnt_bits(int n) { return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
 
-// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from `gptr` land
-// at LDS byte address `lds_base` + 16 i (lds_base wave-uniform, in M0).
+// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from `sbase` +
+// `voff` (a wave-uniform base and a 32-bit per-lane byte offset) land at LDS
+// byte address `lds_base` + 16 i (lds_base wave-uniform, in M0).
 // Issued through asm so that the compiler does not track it: its own wait
 // insertion would otherwise stall the LDS transpose reads of the current stage
 // until this load, aimed at the other stage, completed.  Completion is awaited
 // explicitly (vmcnt) before the barrier that publishes the stage.  M0 has no
 // other user in this kernel (no compiler-issued LDS DMA, no indirect register
 // indexing, no messages), so setting it here disturbs nothing.
-__device__ __forceinline__ void lds_dma16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(gptr), "s"(lds_base) : "memory");
+__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -175,19 +180,39 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   // ---- direct-to-LDS tile load ----
   // Instruction r of wave w fills LDS chunks [64 (w CPW + r), +64): lane l
   // writes chunk p = 64 (w CPW + r) + l, i.e. row p / CPR, physical chunk
-  // p % CPR, which holds logical chunk (p % CPR) ^ swz(row).  Rows past S
-  // re-read row S-1 (in bounds; their scores are masked and their weights 0).
+  // p % CPR, which holds logical chunk (p % CPR) ^ swz(row).  The source is
+  // the wave-uniform base of this (batch, KV head) plus a 32-bit per-lane
+  // byte offset whose tile-independent part is kept per load (one VGPR each).
+  // Rows past S re-read row S-1 (in bounds; their scores are masked and
+  // their weights 0).
+  const bf16* kg = k + kvbase;
+  const bf16* vg = v + kvbase;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  uint32_t koff[CPW], voff[CPW];
+  int lrow[CPW];
+#pragma unroll
+  for (int r = 0; r < CPW; ++r) {
+    const int p = 64 * (wave * CPW + r) + lane;
+    const int row = p / CPR, cph = p % CPR;
+    lrow[r] = row;
+    koff[r] = (uint32_t)(row * D + (cph ^ k_swz<D>(row)) * 8) * 2u;
+    voff[r] = (uint32_t)(row * D + (cph ^ v_swz<D>(row)) * 8) * 2u;
+  }
   auto load_tile = [&](int j, bf16* ks, bf16* vs) {
+    const uint32_t kl = lds_addr(ks) + (uint32_t)(wave_s * CPW) * 1024u;
+    const uint32_t vl = lds_addr(vs) + (uint32_t)(wave_s * CPW) * 1024u;
+    const bool full = (j + 1) * BN <= S;
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
-      const int blk = wave * CPW + r;
-      const int p = 64 * blk + lane;
-      const int row = p / CPR, cph = p % CPR;
-      const int key = min(j * BN + row, S - 1);
-      const bf16* krow = k + kvbase + (size_t)key * D;
-      const bf16* vrow = v + kvbase + (size_t)key * D;
-      lds_dma16(krow + (cph ^ k_swz<D>(row)) * 8, __builtin_amdgcn_readfirstlane(lds_addr(ks + 512 * blk)));
-      lds_dma16(vrow + (cph ^ v_swz<D>(row)) * 8, __builtin_amdgcn_readfirstlane(lds_addr(vs + 512 * blk)));
+      uint32_t add;
+      if (full) {
+        add = (uint32_t)(j * BN * D) * 2u;
+      } else {
+        const int key = min(j * BN + lrow[r], S - 1);
+        add = (uint32_t)((key - lrow[r]) * D) * 2u;
+      }
+      lds_dma16(kg, koff[r] + add, kl + 1024u * r);
+      lds_dma16(vg, voff[r] + add, vl + 1024u * r);
     }
   };
 
@@ -263,11 +288,16 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int kb = 0; kb < NKB; ++kb)
         mx = fmax2(mx, fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), fmax2(s[qb][kb][2], s[qb][kb][3])));
       mx = pair_max32(pair_max16(mx));
-      const float m_new = fmax2(m_run[qb], mx * scale_log2);
+      // The reference maximum only moves when the tile's maximum exceeds it
+      // by more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau
+      // and the accumulator is rarely rescaled; any reference gives the same
+      // O and LSE (it cancels between acc and l), only the rounding changes.
+      const float m_tile = mx * scale_log2;
+      const bool grow = m_tile > m_run[qb] + kLazyTau;   // always when m_run = -inf
+      const float m_new = grow ? m_tile : m_run[qb];
       const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = exp2_hw(m_run[qb] - m_use);
-      // the accumulator only needs rescaling when some row's maximum moved
-      const bool rescale = wave_any(m_new != m_run[qb]);
+      const bool rescale = wave_any(grow);
       m_run[qb] = m_new;
       float rs = 0.f;
 #pragma unroll
