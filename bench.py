@@ -5,21 +5,28 @@ One step = one pass of the whole path on resident synthetic inputs:
   1. causal prefill attn_fwd on the GPT-2-small-shaped workload
      (B=8, H=12, T=S=1024, d=64, bf16; override with --prefill), then
   2. paged decode attn_decode_paged on 64 sequences, 12 query / 2 KV heads,
-     d=128, 16-token pages, lengths U[512, 8192] (split kernel + combine).
+     d=128, 16-token pages, lengths U[512, 8192] (stream kernel + combine).
 
 Reported (one JSON line on stdout):
   value          causal-prefill TFLOP/s = algorithmic FLOPs / mean kernel time
                  (HIP events on the launch stream), FLOPs = 4*d per visible
                  (query, key) pair;
-  decode         paged-decode GB/s = algorithmic bytes / mean time of the split
+  decode         paged-decode GB/s = algorithmic bytes / mean time of the stream
                  + combine kernels, bytes = K+V of every cached token once plus
                  q, o, lse, seq_lens and the used block-table entries;
   roofline       the kernel that takes the most time per step against its
                  published peak (bf16 dense MFMA 2516.6 TFLOP/s, HBM 8 TB/s);
                  `traffic` comes from profiles/counters.json when the measured
                  kernel sources still match the recorded hash, else null;
+  prefill_other  the same causal prefill timing on the two larger prefill
+                 workloads (GQA B=4 T=4096 d=128; long B=1 H=32 T=16384 d=128);
   cpu_baseline   the float64 oracle timed on the host on a bounded sample of
                  the same workloads.
+`--write-counters DIR` turns rocprofv3 FETCH_SIZE / WRITE_SIZE collections
+(DIR/{bench,copy}_{fetch,write}/*_counter_collection.csv, taken on this script
+with the default workload and with --copy-probe) into profiles/counters.json:
+HBM bytes per launch, each counter scaled by what it reads for a copy of
+known size.
 Between steps a 512 MiB buffer is read (summed) so both kernels start with
 cold L2 / Infinity Cache without dirty lines whose write-back would compete
 with them; that read is outside the kernel events but inside ms_per_step.
@@ -124,6 +131,53 @@ def cpu_baseline(pinp, dinp, budget_s):
     }
 
 
+def write_counters(pmc_dir):
+    """profiles/counters.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs."""
+    import csv
+    import glob
+
+    def per_kernel(sub):
+        files = glob.glob(os.path.join(pmc_dir, sub, "*_counter_collection.csv"))
+        if len(files) != 1:
+            raise SystemExit(f"need exactly one counter_collection.csv under {pmc_dir}/{sub}")
+        vals = {}
+        for r in csv.DictReader(open(files[0])):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    copy_bytes = 256 << 20
+    factors = {}
+    for counter, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
+        vals = per_kernel(sub)
+        # the copy is the dispatch with the largest reading (KiB per dispatch)
+        kib = max(max(v) for v in vals.values())
+        factors[counter] = copy_bytes / (kib * 1024.0)
+    fetch, write = per_kernel("bench_fetch"), per_kernel("bench_write")
+
+    def bytes_of(pattern):
+        tot = {}
+        for counter, vals in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
+            kib = sum(sum(v) / len(v) for k, v in vals.items() if any(p in k for p in pattern))
+            tot[counter] = kib * 1024.0 * factors[counter]
+        return tot
+
+    out = {"factors": factors, "copy_probe_bytes": copy_bytes,
+           "commands": {"copy": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
+                                "-- python3 bench.py --copy-probe",
+                        "bench": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
+                                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-flush --no-other-prefill"}}
+    for kind, pattern in (("prefill", ["prefill_bf16_kernel"]),
+                          ("decode", ["decode_stream_kernel", "decode_combine_kernel"])):
+        t = bytes_of(pattern)
+        out[kind] = {"sources_sha": sources_sha(kind), "kernels": pattern,
+                     "fetch_bytes_per_launch": t["FETCH_SIZE"], "write_bytes_per_launch": t["WRITE_SIZE"],
+                     "hbm_bytes_per_launch": t["FETCH_SIZE"] + t["WRITE_SIZE"]}
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def counters_for(kind):
     path = os.path.join(ROOT, "profiles", "counters.json")
     try:
@@ -148,7 +202,14 @@ def main():
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--write-counters", metavar="DIR",
+                    help="write profiles/counters.json from rocprofv3 CSVs under DIR and exit")
+    ap.add_argument("--no-other-prefill", action="store_true",
+                    help="skip the timing of the two larger prefill workloads")
     args = ap.parse_args()
+    if args.write_counters:
+        write_counters(args.write_counters)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -266,6 +327,34 @@ def main():
         "roofline": dict(kernels[dominant]),
         "roofline_per_kernel": kernels,
     }
+    if not args.no_other_prefill:
+        other = {}
+        for name in ("prefill_3", "prefill_4"):
+            if name == pinp.name:
+                continue
+            x = getattr(workloads, name)()
+            xq, xk, xv = (t.to(dev) for t in (x.q, x.k, x.v))
+            xo = torch.empty_like(xq)
+            xl = torch.empty((x.B, x.Hq, x.T), dtype=torch.float32, device=dev)
+            times = []
+            for i in range(7):
+                if flush is not None:
+                    flush.sum()
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                tea.attn_fwd(xq, xk, xv, xo, xl, x.scale, x.causal, stream=stream)
+                b_.record(stream)
+                if i >= 2:
+                    times.append((a, b_))
+            torch.cuda.synchronize()
+            ms = sum(a.elapsed_time(b_) for a, b_ in times) / len(times)
+            fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
+            tf = fl / (ms * 1e-3) / 1e12
+            other[name] = {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal",
+                           "ms": ms, "value": tf, "unit": "TFLOP/s", "frac_of_mfma_peak": tf / peak_p,
+                           "launches": len(times)}
+            del xq, xk, xv, xo, xl
+        out["prefill_other"] = other
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pinp, dinp, args.cpu_budget)
     else:
