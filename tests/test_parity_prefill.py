@@ -69,6 +69,25 @@ def test_small_shapes(case):
     _full_check(inp, name)
 
 
+# Grids of at least 256 workgroups at 128 query rows take the two-blocks-per-
+# wave kernel (the small shapes above take the one-block kernel): non-causal,
+# ragged tails, bottom-right causal with T < S, GQA.
+MEDIUM = [
+    ("medium_noncausal_d128", 2, 8, 8, 2048, 2048, 128, "bf16", False),
+    ("medium_ragged_causal_d64", 3, 12, 4, 1000, 1000, 64, "bf16", True),
+    ("medium_causal_t_lt_s_gqa", 2, 16, 2, 1000, 1500, 128, "bf16", True),
+    ("medium_noncausal_t_gt_s_d64", 1, 32, 8, 1100, 700, 64, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("case", MEDIUM, ids=[c[0] for c in MEDIUM])
+def test_medium_shapes(case):
+    name, B, Hq, Hkv, T, S, d, dtype, causal = case
+    inp = workloads.make_prefill(B, Hq, Hkv, T, S, d, dtype, causal, seed=seed_of(name), name=name)
+    assert ((T + 127) // 128) * B * Hq >= 256
+    _full_check(inp, name)
+
+
 def test_prefill_1_fp32_full():
     _full_check(workloads.prefill_1(), "prefill_1")
 

@@ -36,6 +36,9 @@
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
+#ifndef PREFILL_SMALL_GRID
+#define PREFILL_SMALL_GRID 256    // workgroups at two row blocks per wave
+#endif
 #ifndef PREFILL_D128_WAVES
 #define PREFILL_D128_WAVES 4
 #define PREFILL_D128_BN 64
@@ -108,7 +111,7 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
@@ -117,7 +120,8 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int BN = PrefillCfg<D>::BN;
   constexpr int NST = PrefillCfg<D>::STAGES;
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
-  constexpr int kBM = 32 * PrefillCfg<D>::WAVES;   // query rows per workgroup
+  constexpr int kWR = 16 * QB;               // query rows per wave (QB blocks of 16)
+  constexpr int kBM = kWR * PrefillCfg<D>::WAVES;  // query rows per workgroup
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int NKB = BN / 16;               // 16-key blocks of S^T
   constexpr int NDC = D / 32;                // k-chunks of the S^T MFMA
@@ -168,12 +172,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const size_t kvbase = ((size_t)(b * Hkv + hk) * S) * D;
 
   // ---- keys this workgroup / wave can see ----
-  const int wrow0 = q0 + 32 * wave;                  // first row of this wave
+  const int wrow0 = q0 + kWR * wave;                 // first row of this wave
   const bool wave_live = wrow0 < T;
   int wg_kv_end = S, wave_kv_end = S;                // exclusive
   if (CAUSAL) {
     wg_kv_end = min(S, min(q0 + kBM, T) + (S - T));
-    wave_kv_end = min(S, min(wrow0 + 32, T) + (S - T));
+    wave_kv_end = min(S, min(wrow0 + kWR, T) + (S - T));
   }
   const int ntk = (wg_kv_end + BN - 1) / BN;
 
@@ -217,10 +221,10 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   };
 
   // ---- Q rows into registers (B operand of S^T = K Q^T) ----
-  bf16x8 qop[2][NDC];
-  int row_lim[2];
+  bf16x8 qop[QB][NDC];
+  int row_lim[QB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 16 * qb + l16;
     if (row < T) {
       const bf16* qp = q + qbase + (size_t)row * D + 8 * g;
@@ -235,11 +239,15 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 
   // ---- running softmax state of rows wrow0 + 16 qb + l16 ----
-  float m_run[2] = {-INFINITY, -INFINITY};   // running max of scaled logits, log2 units
-  float l_part[2] = {0.f, 0.f};              // sum over this lane's keys of exp2(s - m_run)
-  f32x4 acc[2][NDB];
+  float m_run[QB], l_part[QB];               // running max of scaled logits (log2 units);
+  f32x4 acc[QB][NDB];                        // sum over this lane's keys of exp2(s - m_run)
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -INFINITY;
+    l_part[qb] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[qb][db] = f32x4{};
 
@@ -252,17 +260,19 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   auto compute_tile = [&](int j, const bf16* ks, const bf16* vs) {
     // S^T[key][row] for the BN keys of this tile; each K operand feeds both row blocks
-    f32x4 s[2][NKB];
+    f32x4 s[QB][NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[0][kb] = s[1][kb] = f32x4{};
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) s[qb][kb] = f32x4{};
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 kop = *reinterpret_cast<const bf16x8*>(
             ks + (16 * kb + l16) * D + (((4 * c + g) ^ kswz) * 8));
-        s[0][kb] = mfma_16x16x32(kop, qop[0][c], s[0][kb]);
-        s[1][kb] = mfma_16x16x32(kop, qop[1][c], s[1][kb]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][kb] = mfma_16x16x32(kop, qop[qb][c], s[qb][kb]);
       }
     }
 
@@ -270,7 +280,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bool need_mask = ((j + 1) * BN > S) || (CAUSAL && (j + 1) * BN - 1 > wrow0 + (S - T));
     if (need_mask) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -282,7 +292,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
     // online softmax update (base 2), per row block
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -320,9 +330,9 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // O^T += V^T P^T, 32 keys at a time; each V operand feeds both row blocks
 #pragma unroll
     for (int c = 0; c < NPC; ++c) {
-      bf16x8 pop[2];
+      bf16x8 pop[QB];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < QB; ++qb)
         pop[qb] = pack_bf16x8(s[qb][2 * c][0], s[qb][2 * c][1], s[qb][2 * c][2], s[qb][2 * c][3],
                               s[qb][2 * c + 1][0], s[qb][2 * c + 1][1], s[qb][2 * c + 1][2],
                               s[qb][2 * c + 1][3]);
@@ -333,8 +343,8 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const i16x4 lo = lds_read_tr16(vp + off);
         const i16x4 hi4 = lds_read_tr16(vp + 16 * D + off);
         const bf16x8 vop = concat_tr(lo, hi4);
-        acc[0][db] = mfma_16x16x32(vop, pop[0], acc[0][db]);
-        acc[1][db] = mfma_16x16x32(vop, pop[1], acc[1][db]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma_16x16x32(vop, pop[qb], acc[qb][db]);
       }
     }
   };
@@ -377,7 +387,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- epilogue: O = acc / l (bf16, nearest even), LSE = ln2 * (m + log2 l) ----
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = pair_sum32(pair_sum16(l_part[qb]));
     const int row = wrow0 + 16 * qb + l16;
     if (row < T) {
@@ -398,18 +408,34 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int QB>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
-  constexpr int kBM = 32 * PrefillCfg<D>::WAVES;
+  constexpr int kBM = 16 * QB * PrefillCfg<D>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S,
                      scale_log2);
   return hipGetLastError();
+}
+
+// Two 16-row blocks per wave share every K and V operand read; one block per
+// wave halves the work on a workgroup's critical path (the longest causal
+// query tile) at the price of twice the LDS reads per MFMA.  A grid of at
+// most one workgroup per CU is bound by that path (B=1 at T=1024, d=64: 11 us
+// instead of 16 us), so it gets one block per wave; a fuller grid is bound by
+// the total work (B=8 at the same shape: 30 us instead of 28.5 us).
+template <int D, bool CAUSAL>
+hipError_t launch_rows(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
+  constexpr int kBM2 = 32 * PrefillCfg<D>::WAVES;
+  const long long wgs2 = (long long)((T + kBM2 - 1) / kBM2) * B * Hq;
+  if (wgs2 < PREFILL_SMALL_GRID)
+    return launch_one<D, CAUSAL, 1>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+  return launch_one<D, CAUSAL, 2>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
 }
 
 }  // namespace
@@ -418,10 +444,10 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int B, int Hq, int Hkv, int T, int S, int d, float scale_log2,
                                bool causal, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_one<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                  : launch_one<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
-  return causal ? launch_one<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                : launch_one<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+    return causal ? launch_rows<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
+                  : launch_rows<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+  return causal ? launch_rows<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
+                : launch_rows<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
 }
 
 }  // namespace attn
