@@ -1,12 +1,15 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) tiled exact attention library.
  *
- * Two operations, each computing exactly softmax(scale * Q K^T) V without the
- * score matrix ever reaching device memory:
+ * Three operations, each computing exactly softmax(scale * Q K^T) V, or its
+ * gradients, without the score matrix ever reaching device memory:
  *
  *   attn_fwd           prefill: every query row of a sequence against its keys,
  *                      optionally causal, with grouped-query heads, writing O
  *                      and the per-row log-sum-exp.
+ *   attn_bwd           the gradients dQ, dK, dV of attn_fwd's output for a
+ *                      given output gradient dO, rebuilding the probabilities
+ *                      tile by tile from the saved log-sum-exp.
  *   attn_decode_paged  decode: one query token per sequence against a key/value
  *                      cache stored in fixed-size pages reached through a
  *                      block table.
@@ -84,13 +87,53 @@ typedef enum {
  * nearest even from float32.
  *
  * Requirements: B, Hq, Hkv, T, S >= 1; Hq % Hkv == 0; causal implies T <= S;
- * scale finite and > 0; q, k, v, o 16-byte aligned, lse 4-byte aligned;
- * o and lse must not overlap q, k, v or each other.  d must be 64 or 128 (else
- * ATTN_EUNSUPPORTED); dtype ATTN_F32 or ATTN_BF16.
+ * T * d and S * d below 2^31; scale finite and > 0; q, k, v, o 16-byte
+ * aligned, lse 4-byte aligned; o and lse must not overlap q, k, v or each
+ * other.  d must be 64 or 128 (else ATTN_EUNSUPPORTED); dtype ATTN_F32 or
+ * ATTN_BF16.
  */
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
              int dtype, void* stream);
+
+/*
+ * attn_bwd -- gradients of attn_fwd.
+ *
+ *   q, k, v, o, lse   as for attn_fwd; o and lse are what attn_fwd wrote for
+ *                     these q, k, v, scale and causal (lse may not be NULL)
+ *   dout [B, Hq,  T, d]  bf16     gradient of the loss with respect to o
+ *   dq   [B, Hq,  T, d]  bf16     gradient with respect to q (written)
+ *   dk   [B, Hkv, S, d]  bf16     gradient with respect to k (written)
+ *   dv   [B, Hkv, S, d]  bf16     gradient with respect to v (written)
+ *   workspace  >= attn_bwd_workspace_size(B, Hq, T) bytes of device memory,
+ *              16-byte aligned: per-row scratch, contents on entry ignored.
+ *              Calls that share a workspace must not overlap in time.
+ *
+ * "Advanced Attention Mechanisms - II" (A. Das), section "Flash Attention":
+ * the attention matrix is not kept for the backward pass, only the row
+ * statistics, so the probabilities are recomputed per tile:
+ *   P = exp(scale q_i . k_j - lse_i) on visible (i, j), else 0;
+ *   D_i = sum_c dout[i,c] o[i,c];  dS = P * (dout V^T - D);
+ *   dv = P^T dout,  dq = scale dS k,  dk = scale dS^T q,
+ * the derivative of attn_fwd's definition (same mask and head mapping).  A KV
+ * head's dk and dv sum the contributions of all Hq / Hkv query heads that
+ * read it, in a fixed order; no atomics are used, so equal inputs give
+ * bitwise equal results.  Accumulation is float32; outputs are rounded to
+ * nearest even bf16.
+ *
+ * Requirements: as for attn_fwd, plus: dtype must be ATTN_BF16 (else
+ * ATTN_EUNSUPPORTED); every pointer non-NULL; dout, dq, dk, dv and workspace
+ * 16-byte aligned; dq, dk, dv and workspace must not overlap each other or
+ * any input.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv,
+             int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
+             int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace attn_bwd needs (0 if invalid): B * Hq * T floats
+ * (the per-row D above), rounded up to a multiple of 256. */
+size_t attn_bwd_workspace_size(int B, int Hq, int T);
 
 /*
  * attn_decode_paged -- one query token per sequence against a paged KV cache.

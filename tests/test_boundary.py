@@ -25,8 +25,9 @@ def _declared_functions():
 
 
 def test_header_declares_the_expected_entry_points():
-    assert _declared_functions() == ["attn_decode_paged", "attn_decode_workspace_size", "attn_fwd",
-                                     "attn_last_error", "attn_status_string"]
+    assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
+                                     "attn_decode_workspace_size", "attn_fwd", "attn_last_error",
+                                     "attn_status_string"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -105,6 +106,60 @@ def test_fwd_rejects_bad_arguments(bad, code):
 def test_fwd_f32_shares_the_checks():
     assert _fwd(dtype=ATTN_F32, d=80) == ATTN_EUNSUPPORTED
     assert _fwd(dtype=ATTN_F32, T=100, S=50) == ATTN_EINVAL
+
+
+def test_fwd_rejects_heads_past_32_bit_offsets():
+    assert _fwd(T=1 << 24, S=1 << 24, d=128, B=1, Hq=1, Hkv=1, causal=0) == ATTN_EINVAL
+    assert "2^31" in tea.attn_last_error()
+
+
+# --- attn_bwd argument checks ---------------------------------------------------
+
+def test_bwd_workspace_size_formula():
+    assert tea.attn_bwd_workspace_size(4, 12, 4096) == 4 * 12 * 4096 * 4
+    assert tea.attn_bwd_workspace_size(1, 1, 1) == 256
+    assert tea.attn_bwd_workspace_size(1, 3, 7) == 256
+    assert tea.attn_bwd_workspace_size(1, 1, 65) == 512
+    assert tea.attn_bwd_workspace_size(0, 1, 1) == 0
+    assert tea.attn_bwd_workspace_size(1, 1, 0) == 0
+
+
+BWD_WS = tea.attn_bwd_workspace_size(1, 4, 64)
+BWD_OK = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, do=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
+              B=1, Hq=4, Hkv=2, T=64, S=64, d=64, scale=0.125, causal=1, dtype=ATTN_BF16,
+              ws=10 * P, ws_bytes=BWD_WS, stream=None)
+
+
+def _bwd(**kw):
+    a = dict(BWD_OK)
+    a.update(kw)
+    return tea.lib().attn_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                              a["dv"], a["B"], a["Hq"], a["Hkv"], a["T"], a["S"], a["d"], a["scale"],
+                              a["causal"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), ATTN_EINVAL), (dict(lse=None), ATTN_EINVAL), (dict(do=None), ATTN_EINVAL),
+    (dict(dq=None), ATTN_EINVAL), (dict(dk=None), ATTN_EINVAL), (dict(dv=None), ATTN_EINVAL),
+    (dict(ws=None), ATTN_EINVAL),
+    (dict(B=0), ATTN_EINVAL), (dict(T=0), ATTN_EINVAL), (dict(S=0), ATTN_EINVAL),
+    (dict(Hq=6, Hkv=4), ATTN_EINVAL),
+    (dict(T=65, S=64, causal=1), ATTN_EINVAL),
+    (dict(scale=0.0), ATTN_EINVAL), (dict(scale=float("nan")), ATTN_EINVAL),
+    (dict(dtype=ATTN_F32), ATTN_EUNSUPPORTED), (dict(dtype=9), ATTN_EUNSUPPORTED),
+    (dict(d=96), ATTN_EUNSUPPORTED),
+    (dict(do=6 * P + 8), ATTN_EINVAL), (dict(dk=8 * P + 2), ATTN_EINVAL),
+    (dict(lse=5 * P + 2), ATTN_EINVAL), (dict(ws=10 * P + 4), ATTN_EINVAL),
+    (dict(ws_bytes=BWD_WS - 1), ATTN_EINVAL),
+    (dict(dq=P), ATTN_EINVAL),                   # dq aliases q
+    (dict(dv=6 * P + 256), ATTN_EINVAL),         # dv inside dO
+    (dict(dk=7 * P + 512), ATTN_EINVAL),         # dk inside dq
+    (dict(ws=9 * P), ATTN_EINVAL),               # workspace aliases dv
+    (dict(T=1 << 24, S=1 << 24, d=128, causal=0, ws_bytes=1 << 40), ATTN_EINVAL),   # 32-bit offsets
+])
+def test_bwd_rejects_bad_arguments(bad, code):
+    assert _bwd(**bad) == code
+    assert tea.attn_last_error().startswith("attn_bwd")
 
 
 # --- attn_decode_paged argument checks ------------------------------------------

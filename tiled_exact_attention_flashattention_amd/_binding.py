@@ -74,6 +74,11 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, vp, sz, vp]
     L.attn_decode_paged.restype = i32
+    L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
+                           i32, i32, vp, sz, vp]
+    L.attn_bwd.restype = i32
+    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    L.attn_bwd_workspace_size.restype = sz
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.attn_decode_workspace_size.restype = sz
     L.attn_status_string.argtypes = [i32]
@@ -94,6 +99,10 @@ def attn_last_error() -> str:
 
 def attn_decode_workspace_size(N: int, Hq: int, d: int, max_blocks: int, page: int = PAGE) -> int:
     return int(lib().attn_decode_workspace_size(N, Hq, d, max_blocks, page))
+
+
+def attn_bwd_workspace_size(B: int, Hq: int, T: int) -> int:
+    return int(lib().attn_bwd_workspace_size(B, Hq, T))
 
 
 def _check(status: int) -> None:
@@ -154,6 +163,34 @@ def attn_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     _check(st)
 
 
+def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, workspace,
+             stream=None) -> None:
+    """Enqueue attn_bwd on ``stream`` (default: the current stream of q's device).
+
+    q/o/dout/dq [B,Hq,T,d], k/v/dk/dv [B,Hkv,S,d], all bf16; lse [B,Hq,T]
+    float32 from attn_fwd; workspace: a device tensor of at least
+    attn_bwd_workspace_size bytes.
+    """
+    import torch
+    _require_device_tensors(q, k, v, o, lse, dout, dq, dk, dv, workspace)
+    B, Hq, T, d = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, S, d) or v.shape != k.shape or dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("k, v, dk, dv must be [B, Hkv, S, d]")
+    if o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("o, dout, dq must have q's shape")
+    if len({t.dtype for t in (q, k, v, o, dout, dq, dk, dv)}) != 1:
+        raise TypeError("q, k, v, o, dout, dq, dk, dv must share one dtype")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, T):
+        raise ValueError("lse must be float32 [B, Hq, T]")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                        dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                        B, Hq, Hkv, T, S, d, float(scale), int(bool(causal)), _dtype_code(q),
+                        workspace.data_ptr(), ws_bytes, _stream_ptr(q.device, stream))
+    _check(st)
+
+
 def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: float,
                       workspace, page: int = PAGE, stream=None) -> None:
     """Enqueue attn_decode_paged on ``stream``.
@@ -195,6 +232,21 @@ def fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, with_lse: 
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
     attn_fwd(q, k, v, o, lse, scale, causal)
     return o, lse
+
+
+def bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = False,
+        workspace=None):
+    """Allocate dQ, dK, dV (and the workspace if not given) and run attn_bwd."""
+    import torch
+    B, Hq, T, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace_size(B, Hq, T), dtype=torch.uint8,
+                                device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, causal, workspace)
+    return dq, dk, dv
 
 
 def decode_workspace(N: int, Hq: int, d: int, max_blocks: int, device) -> "object":

@@ -43,6 +43,8 @@ bool overlap(const void* p, size_t n, const void* q, size_t m) {
 constexpr int kPage = 16;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int64_t kMaxElems = (int64_t)1 << 40;
+// One head's rows are addressed with 32-bit element offsets inside the kernels.
+constexpr int64_t kMaxHeadElems = (int64_t)1 << 31;
 
 size_t round256(int64_t x) { return (size_t)((x + 255) / 256 * 256); }
 
@@ -77,6 +79,11 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
+size_t attn_bwd_workspace_size(int B, int Hq, int T) {
+  if (B < 1 || Hq < 1 || T < 1) return 0;
+  return round256((int64_t)B * Hq * T * 4);
+}
+
 size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page) {
   if (N < 1 || Hq < 1 || d < 1 || max_blocks < 1 || page != kPage) return 0;
   return decode_workspace_layout(N, Hq, d).total;
@@ -101,6 +108,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return fail(ATTN_EINVAL, "attn_fwd: q/k/v/o need 16-byte alignment, lse 4-byte");
   const int64_t qn = (int64_t)B * Hq * T * d, kn = (int64_t)B * Hkv * S * d;
   if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "attn_fwd: tensor too large");
+  if ((int64_t)T * d >= kMaxHeadElems || (int64_t)S * d >= kMaxHeadElems)
+    return fail(ATTN_EINVAL, "attn_fwd: T*d and S*d must be below 2^31");
   const int64_t grid = ((int64_t)T + 127) / 128 * B * Hq;
   if (grid > 0x7fffffff) return fail(ATTN_EINVAL, "attn_fwd: too many query tiles");
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
@@ -118,6 +127,58 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
                      : attn::launch_prefill_f32(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale_log2,
                                                 causal != 0, st);
   if (e != hipSuccess) return fail(ATTN_EHIP, "attn_fwd: %s", hipGetErrorString(e));
+  return ATTN_OK;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+             const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int T, int S,
+             int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
+             void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
+    return fail(ATTN_EINVAL, "attn_bwd: every pointer must be non-NULL");
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1)
+    return fail(ATTN_EINVAL, "attn_bwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d T=%d S=%d d=%d)", B,
+                Hq, Hkv, T, S, d);
+  if (Hq % Hkv != 0) return fail(ATTN_EINVAL, "attn_bwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (causal && T > S)
+    return fail(ATTN_EINVAL, "attn_bwd: causal attention needs T <= S (T=%d S=%d)", T, S);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "attn_bwd: scale must be finite and > 0");
+  if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "attn_bwd: only bf16 is supported");
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "attn_bwd: head dim %d (need 64 or 128)", d);
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
+      !aligned(dout, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) ||
+      !aligned(lse, 4) || !aligned(workspace, 16))
+    return fail(ATTN_EINVAL, "attn_bwd: tensors need 16-byte alignment, lse 4-byte");
+  const int64_t qn = (int64_t)B * Hq * T * d, kn = (int64_t)B * Hkv * S * d;
+  if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "attn_bwd: tensor too large");
+  if ((int64_t)T * d >= kMaxHeadElems || (int64_t)S * d >= kMaxHeadElems)
+    return fail(ATTN_EINVAL, "attn_bwd: T*d and S*d must be below 2^31");
+  if (((int64_t)T + 127) / 128 * B * Hq > 0x7fffffff || ((int64_t)S + 63) / 64 * B * Hkv > 0x7fffffff ||
+      ((int64_t)B * Hq * T + 15) / 16 > 0x7fffffff)
+    return fail(ATTN_EINVAL, "attn_bwd: too many tiles");
+  const size_t need = attn_bwd_workspace_size(B, Hq, T);
+  if (workspace_bytes < need)
+    return fail(ATTN_EINVAL, "attn_bwd: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  const size_t qb = (size_t)qn * 2, kb = (size_t)kn * 2, lb = (size_t)B * Hq * T * 4;
+  const void* ins[] = {q, k, v, o, lse, dout};
+  const size_t in_bytes[] = {qb, kb, kb, qb, lb, qb};
+  void* outs[] = {dq, dk, dv, workspace};
+  const size_t out_bytes[] = {qb, kb, kb, need};
+  for (int a = 0; a < 4; ++a) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(outs[a], out_bytes[a], ins[i], in_bytes[i]))
+        return fail(ATTN_EINVAL, "attn_bwd: dq/dk/dv/workspace overlap an input");
+    for (int c = a + 1; c < 4; ++c)
+      if (overlap(outs[a], out_bytes[a], outs[c], out_bytes[c]))
+        return fail(ATTN_EINVAL, "attn_bwd: dq, dk, dv and workspace must not overlap");
+  }
+
+  hipError_t e = attn::launch_backward_bf16(q, k, v, o, lse, dout, dq, dk, dv,
+                                            static_cast<float*>(workspace), B, Hq, Hkv, T, S, d,
+                                            scale, causal != 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_bwd: %s", hipGetErrorString(e));
   return ATTN_OK;
 }
 

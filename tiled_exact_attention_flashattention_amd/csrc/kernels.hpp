@@ -37,4 +37,11 @@ hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
                                float scale_log2, hipStream_t stream);
 
+// Backward, bf16 in/out, fp32 accumulation on MFMA: D = rowsum(dO * O) into
+// `dsum` [B*Hq*T] floats, then dQ, then dK and dV (three launches, no atomics).
+hipError_t launch_backward_bf16(const void* q, const void* k, const void* v, const void* o,
+                                const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                float* dsum, int B, int Hq, int Hkv, int T, int S, int d,
+                                float scale, bool causal, hipStream_t stream);
+
 }  // namespace attn

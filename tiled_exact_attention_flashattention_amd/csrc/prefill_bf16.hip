@@ -35,6 +35,7 @@
 //     so its K/V is re-read from that XCD's L2.
 #include "cdna4.hpp"
 #include "kernels.hpp"
+#include "lds_stage.hpp"
 
 #ifndef PREFILL_SMALL_GRID
 #define PREFILL_SMALL_GRID 256    // workgroups at two row blocks per wave
@@ -75,41 +76,6 @@ __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) 
 // Slack of the running maximum (log2 units): P = exp2(s - m) may reach
 // 2^kLazyTau, far inside bf16 and fp32 range.
 constexpr float kLazyTau = 8.f;
-
-// s_waitcnt encodings (gfx9): vmcnt in bits [3:0] and [15:14], expcnt in
-// [6:4], lgkmcnt in [11:8].  kWaitLgkm0 | vmcnt_bits(n) waits for lgkmcnt(0)
-// and vmcnt(n) with expcnt unconstrained.
-constexpr unsigned kWaitLgkm0 = 0x0070;
-constexpr unsigned kWaitVm0Lgkm0 = 0x0070;
-constexpr unsigned vmcnt_bits(int n) { return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
-
-// One 16-byte-per-lane direct-to-LDS load: lane i's 16 bytes from `sbase` +
-// `voff` (a wave-uniform base and a 32-bit per-lane byte offset) land at LDS
-// byte address `lds_base` + 16 i (lds_base wave-uniform, in M0).
-// Issued through asm so that the compiler does not track it: its own wait
-// insertion would otherwise stall the LDS transpose reads of the current stage
-// until this load, aimed at the other stage, completed.  Completion is awaited
-// explicitly (vmcnt) before the barrier that publishes the stage.  M0 has no
-// other user in this kernel (no compiler-issued LDS DMA, no indirect register
-// indexing, no messages), so setting it here disturbs nothing.
-__device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
-// Workgroup barrier without a memory fence: the LDS stages are filled by the
-// direct-to-LDS loads, whose completion is awaited explicitly with vmcnt, and
-// a fence here would make the compiler wait for the load in flight as well.
-// The empty asm statements keep the optimiser from moving LDS accesses across.
-__device__ __forceinline__ void stage_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int D, bool CAUSAL, int QB>
 __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
@@ -358,7 +324,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     if (NST == 3 && j + 1 < ntk) {
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(2 * CPW));
     } else {
-      __builtin_amdgcn_s_waitcnt(kWaitVm0Lgkm0);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));
     }
     stage_barrier();
     if (j + NST - 1 < ntk) load_tile(j + NST - 1, kn, vn);

@@ -26,6 +26,11 @@ prefill_4  B=1, Hq=Hkv=32, T=S=16384, d=128, bf16, causal, x0.5, seed 1004
 decode_5   64 sequences, Hq=12, Hkv=2, d=128, bf16, lengths U[512, 8192],
            16-token pages, seed 1005
 ========  =====================================================================
+
+Backward inputs (``make_backward``) draw q, k, v exactly as ``make_prefill``
+and then the output gradient dO, float32 ``standard_normal`` of q's shape,
+rounded to bf16.  ``backward_3`` is the gradient pass of prefill_3: its q, k,
+v are prefill_3's (same seed), with dO drawn after them.
 """
 from __future__ import annotations
 
@@ -56,6 +61,14 @@ class PrefillInputs:
     def f64(self):
         """The exact input values widened to float64 numpy arrays."""
         return (self.q.double().numpy(), self.k.double().numpy(), self.v.double().numpy())
+
+
+@dataclass
+class BackwardInputs(PrefillInputs):
+    do: object = None   # torch CPU tensor [B,Hq,T,d]: gradient of the loss w.r.t. O
+
+    def f64(self):
+        return super().f64() + (self.do.double().numpy(),)
 
 
 @dataclass
@@ -109,6 +122,24 @@ def make_prefill(B, Hq, Hkv, T, S, d, dtype="bf16", causal=True, seed=0,
         scale = 1.0 / math.sqrt(d)
     return PrefillInputs(B, Hq, Hkv, T, S, d, dtype, bool(causal), float(scale),
                          _cast(q, dtype), _cast(k, dtype), _cast(v, dtype), name=name)
+
+
+def make_backward(B, Hq, Hkv, T, S, d, causal=True, seed=0, amplitude=1.0, scale=None,
+                  name="") -> BackwardInputs:
+    """q, k, v exactly as ``make_prefill`` (bf16), then dO iid N(0,1) [B,Hq,T,d]."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, T, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, S, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, S, d), dtype=np.float32)
+    if amplitude != 1.0:
+        a = np.float32(amplitude)
+        q, k, v = q * a, k * a, v * a
+    do = rng.standard_normal((B, Hq, T, d), dtype=np.float32)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return BackwardInputs(B, Hq, Hkv, T, S, d, "bf16", bool(causal), float(scale),
+                          _cast(q, "bf16"), _cast(k, "bf16"), _cast(v, "bf16"), name=name,
+                          do=_cast(do, "bf16"))
 
 
 def make_decode(N, Hq, Hkv, d, min_len, max_len, page=PAGE, max_blocks=None, seed=0,
@@ -178,12 +209,18 @@ def decode_5(poison_tail=False):
                        poison_tail=poison_tail, name="decode_5")
 
 
+def backward_3():
+    """The gradient pass of prefill_3 (same q, k, v), dO drawn after v."""
+    return make_backward(4, 12, 2, 4096, 4096, 128, causal=True, seed=1003, name="backward_3")
+
+
 WORKLOADS = {
     "prefill_1": prefill_1,
     "prefill_2": prefill_2,
     "prefill_3": prefill_3,
     "prefill_4": prefill_4,
     "decode_5": decode_5,
+    "backward_3": backward_3,
 }
 
 # Human-readable shapes, used for labels in the benchmark output.
@@ -193,4 +230,5 @@ SHAPES = {
     "prefill_3": dict(B=4, Hq=12, Hkv=2, T=4096, S=4096, d=128, dtype="bf16", causal=True),
     "prefill_4": dict(B=1, Hq=32, Hkv=32, T=16384, S=16384, d=128, dtype="bf16", causal=True),
     "decode_5": dict(N=64, Hq=12, Hkv=2, d=128, page=16, min_len=512, max_len=8192, dtype="bf16"),
+    "backward_3": dict(B=4, Hq=12, Hkv=2, T=4096, S=4096, d=128, dtype="bf16", causal=True),
 }
