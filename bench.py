@@ -20,6 +20,12 @@ Reported (one JSON line on stdout):
                  kernel sources still match the recorded hash, else null;
   prefill_other  the same causal prefill timing on the two larger prefill
                  workloads (GQA B=4 T=4096 d=128; long B=1 H=32 T=16384 d=128);
+  backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
+                 kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
+                 T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
+                 (query, key) pair (recomputed scores, dP, dV, dQ, dK: five
+                 products of 2*d each), next to the float64 backward oracle
+                 timed on a bounded sample of its heads;
   cpu_baseline   the float64 oracle timed on the host on a bounded sample of
                  the same workloads.
 `--write-counters DIR` turns rocprofv3 FETCH_SIZE / WRITE_SIZE collections
@@ -131,6 +137,55 @@ def cpu_baseline(pinp, dinp, budget_s):
     }
 
 
+def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
+    """Time attn_bwd on backward_3 (7 cold launches, the first 2 untimed)."""
+    import torch
+    x = workloads.backward_3()
+    xq, xk, xv, xdo = (t.to(dev) for t in (x.q, x.k, x.v, x.do))
+    xo, xl = tea.fwd(xq, xk, xv, scale=x.scale, causal=x.causal)
+    gq, gk, gv = torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv)
+    ws = torch.empty(tea.attn_bwd_workspace_size(x.B, x.Hq, x.Hkv, x.T, x.S, x.d), dtype=torch.uint8,
+                     device=dev)
+    times = []
+    for i in range(7):
+        if flush is not None:
+            flush.sum()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        tea.attn_bwd(xq, xk, xv, xo, xl, xdo, gq, gk, gv, x.scale, x.causal, ws, stream=stream)
+        b_.record(stream)
+        if i >= 2:
+            times.append((a, b_))
+    torch.cuda.synchronize()
+    ms = sum(a.elapsed_time(b_) for a, b_ in times) / len(times)
+    fwd_flops, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
+    flops = fwd_flops // 4 * 10
+    tf = flops / (ms * 1e-3) / 1e12
+    rec = {"config": f"{x.name}: B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal",
+           "kernels": "bwd_prep_kernel+bwd_dq_kernel+bwd_dkdv_kernel", "ms": ms, "value": tf,
+           "unit": "TFLOP/s", "algorithmic_flops": flops, "bound": "mfma",
+           "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS,
+           "launches": len(times), "cpu_baseline": None}
+    del xq, xk, xv, xdo, xo, xl, gq, gk, gv, ws
+    if cpu_budget_s:
+        import oracle
+        g = x.Hq // x.Hkv
+        head_flops = flops // (x.B * x.Hq)
+        done, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < cpu_budget_s:
+            b, h = divmod(done % (x.B * x.Hq), x.Hq)
+            oracle.attention_head_backward(x.q[b, h].double().numpy(), x.k[b, h // g].double().numpy(),
+                                           x.v[b, h // g].double().numpy(), x.do[b, h].double().numpy(),
+                                           x.scale, x.causal)
+            done += 1
+        tc = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": done * head_flops / tc / 1e12, "unit": "TFLOP/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{done} (batch, head) gradient problems of {x.name} "
+                                         f"({tc:.1f} s)"}
+    return rec
+
+
 def write_counters(pmc_dir):
     """profiles/counters.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs."""
     import csv
@@ -206,6 +261,7 @@ def main():
                     help="write profiles/counters.json from rocprofv3 CSVs under DIR and exit")
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the timing of the two larger prefill workloads")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     args = ap.parse_args()
     if args.write_counters:
         write_counters(args.write_counters)
@@ -355,6 +411,9 @@ def main():
                            "launches": len(times)}
             del xq, xk, xv, xo, xl
         out["prefill_other"] = other
+    if not args.no_backward:
+        out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
+                                         None if args.no_cpu_baseline else args.cpu_budget / 3)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(pinp, dinp, args.cpu_budget)
     else:

@@ -105,8 +105,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  *   dq   [B, Hq,  T, d]  bf16     gradient with respect to q (written)
  *   dk   [B, Hkv, S, d]  bf16     gradient with respect to k (written)
  *   dv   [B, Hkv, S, d]  bf16     gradient with respect to v (written)
- *   workspace  >= attn_bwd_workspace_size(B, Hq, T) bytes of device memory,
- *              16-byte aligned: per-row scratch, contents on entry ignored.
+ *   workspace  >= attn_bwd_workspace_size(B, Hq, Hkv, T, S, d) bytes of
+ *              device memory, 16-byte aligned: per-row statistics and
+ *              partial dK/dV, contents on entry ignored.
  *              Calls that share a workspace must not overlap in time.
  *
  * "Advanced Attention Mechanisms - II" (A. Das), section "Flash Attention":
@@ -131,9 +132,16 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
              int dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace attn_bwd needs (0 if invalid): B * Hq * T floats
- * (the per-row D above), rounded up to a multiple of 256. */
-size_t attn_bwd_workspace_size(int B, int Hq, int T);
+/* Bytes of workspace attn_bwd needs (0 if invalid): r(2 * B * Hq * T floats)
+ * (per query row, its log-sum-exp in base 2 and D above), r() rounding up to
+ * a multiple of 256, plus 2 * n * B * Hkv * S * d floats when n > 1, where n,
+ * the number of workgroups that share the query heads of one KV head in the
+ * dK/dV pass, is the smallest divisor of Hq / Hkv with
+ * ceil(S / 128) * B * Hkv * n >= 512 (Hq / Hkv if there is none): their fp32
+ * partial dK and dV, summed in a fixed order at the end.  About 67 MB at
+ * B=4, Hq=12, Hkv=2, T=S=4096, d=128 (n = 2); 0.4 MB with n = 1 at B=8,
+ * Hq=Hkv=12, T=S=1024, d=64. */
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int T, int S, int d);
 
 /*
  * attn_decode_paged -- one query token per sequence against a paged KV cache.

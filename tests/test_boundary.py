@@ -115,16 +115,26 @@ def test_fwd_rejects_heads_past_32_bit_offsets():
 
 # --- attn_bwd argument checks ---------------------------------------------------
 
+def _bwd_ws(B, Hq, Hkv, T, S, d):
+    """Layout documented in include/attn.h: row statistics, then head-split partials."""
+    hpg, base = Hq // Hkv, -(-S // 128) * B * Hkv
+    n = next((m for m in range(1, hpg + 1) if hpg % m == 0 and base * m >= 512), hpg)
+    return _r256(B * Hq * T * 8) + (2 * n * B * Hkv * S * d * 4 if n > 1 else 0)
+
+
 def test_bwd_workspace_size_formula():
-    assert tea.attn_bwd_workspace_size(4, 12, 4096) == 4 * 12 * 4096 * 4
-    assert tea.attn_bwd_workspace_size(1, 1, 1) == 256
-    assert tea.attn_bwd_workspace_size(1, 3, 7) == 256
-    assert tea.attn_bwd_workspace_size(1, 1, 65) == 512
-    assert tea.attn_bwd_workspace_size(0, 1, 1) == 0
-    assert tea.attn_bwd_workspace_size(1, 1, 0) == 0
+    assert tea.attn_bwd_workspace_size(4, 12, 2, 4096, 4096, 128) == 68681728   # 2 head splits
+    assert tea.attn_bwd_workspace_size(8, 12, 12, 1024, 1024, 64) == 786432      # no split
+    for args in [(4, 12, 2, 4096, 4096, 128), (8, 12, 12, 1024, 1024, 64), (1, 1, 1, 1, 1, 64),
+                 (1, 32, 4, 100, 100, 128), (2, 12, 4, 777, 1500, 64), (3, 6, 1, 10, 3000, 128)]:
+        assert tea.attn_bwd_workspace_size(*args) == _bwd_ws(*args), args
+    assert tea.attn_bwd_workspace_size(1, 1, 1, 1, 1, 64) == 256
+    assert tea.attn_bwd_workspace_size(0, 1, 1, 1, 1, 64) == 0
+    assert tea.attn_bwd_workspace_size(1, 1, 1, 0, 1, 64) == 0
+    assert tea.attn_bwd_workspace_size(1, 6, 4, 8, 8, 64) == 0      # Hq not a multiple of Hkv
 
 
-BWD_WS = tea.attn_bwd_workspace_size(1, 4, 64)
+BWD_WS = tea.attn_bwd_workspace_size(1, 4, 2, 64, 64, 64)
 BWD_OK = dict(q=P, k=2 * P, v=3 * P, o=4 * P, lse=5 * P, do=6 * P, dq=7 * P, dk=8 * P, dv=9 * P,
               B=1, Hq=4, Hkv=2, T=64, S=64, d=64, scale=0.125, causal=1, dtype=ATTN_BF16,
               ws=10 * P, ws_bytes=BWD_WS, stream=None)

@@ -119,7 +119,7 @@ def test_repeat_runs_are_bitwise_identical():
 def test_workspace_contents_are_ignored():
     inp = workloads.make_backward(1, 4, 2, 300, 300, 64, True, seed=8, name="bwd_ws")
     announce("attn_bwd workspace zero vs 0xff")
-    nbytes = tea.attn_bwd_workspace_size(inp.B, inp.Hq, inp.T)
+    nbytes = tea.attn_bwd_workspace_size(inp.B, inp.Hq, inp.Hkv, inp.T, inp.S, inp.d)
     ws0 = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     ws1 = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
     for a, b in zip(_run(inp, ws0), _run(inp, ws1)):

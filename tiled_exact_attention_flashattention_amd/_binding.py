@@ -77,7 +77,7 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                            i32, i32, vp, sz, vp]
     L.attn_bwd.restype = i32
-    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32]
+    L.attn_bwd_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     L.attn_bwd_workspace_size.restype = sz
     L.attn_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
     L.attn_decode_workspace_size.restype = sz
@@ -101,8 +101,8 @@ def attn_decode_workspace_size(N: int, Hq: int, d: int, max_blocks: int, page: i
     return int(lib().attn_decode_workspace_size(N, Hq, d, max_blocks, page))
 
 
-def attn_bwd_workspace_size(B: int, Hq: int, T: int) -> int:
-    return int(lib().attn_bwd_workspace_size(B, Hq, T))
+def attn_bwd_workspace_size(B: int, Hq: int, Hkv: int, T: int, S: int, d: int) -> int:
+    return int(lib().attn_bwd_workspace_size(B, Hq, Hkv, T, S, d))
 
 
 def _check(status: int) -> None:
@@ -242,8 +242,8 @@ def bwd(q, k, v, o, lse, dout, scale: Optional[float] = None, causal: bool = Fal
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if workspace is None:
-        workspace = torch.empty(attn_bwd_workspace_size(B, Hq, T), dtype=torch.uint8,
-                                device=q.device)
+        workspace = torch.empty(attn_bwd_workspace_size(B, Hq, k.shape[1], T, k.shape[2], d),
+                                dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale, causal, workspace)
     return dq, dk, dv

@@ -79,9 +79,9 @@ const char* attn_status_string(int status) {
 
 const char* attn_last_error(void) { return g_last_error; }
 
-size_t attn_bwd_workspace_size(int B, int Hq, int T) {
-  if (B < 1 || Hq < 1 || T < 1) return 0;
-  return round256((int64_t)B * Hq * T * 4);
+size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int T, int S, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1 || Hq % Hkv != 0) return 0;
+  return round256((int64_t)B * Hq * T * 8) + attn::bwd_kv_part_bytes(B, Hq, Hkv, S, d);
 }
 
 size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page) {
@@ -154,10 +154,10 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "attn_bwd: tensor too large");
   if ((int64_t)T * d >= kMaxHeadElems || (int64_t)S * d >= kMaxHeadElems)
     return fail(ATTN_EINVAL, "attn_bwd: T*d and S*d must be below 2^31");
-  if (((int64_t)T + 127) / 128 * B * Hq > 0x7fffffff || ((int64_t)S + 63) / 64 * B * Hkv > 0x7fffffff ||
+  if (((int64_t)T + 127) / 128 * B * Hq > 0x7fffffff || ((int64_t)S + 127) / 128 * B * Hq > 0x7fffffff ||
       ((int64_t)B * Hq * T + 15) / 16 > 0x7fffffff)
     return fail(ATTN_EINVAL, "attn_bwd: too many tiles");
-  const size_t need = attn_bwd_workspace_size(B, Hq, T);
+  const size_t need = attn_bwd_workspace_size(B, Hq, Hkv, T, S, d);
   if (workspace_bytes < need)
     return fail(ATTN_EINVAL, "attn_bwd: workspace of %zu bytes needed, %zu given", need,
                 workspace_bytes);
@@ -175,9 +175,15 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
         return fail(ATTN_EINVAL, "attn_bwd: dq, dk, dv and workspace must not overlap");
   }
 
-  hipError_t e = attn::launch_backward_bf16(q, k, v, o, lse, dout, dq, dk, dv,
-                                            static_cast<float*>(workspace), B, Hq, Hkv, T, S, d,
-                                            scale, causal != 0, static_cast<hipStream_t>(stream));
+  attn::BwdWorkspace bw;
+  bw.stats = static_cast<float*>(workspace);
+  bw.kv_part = attn::bwd_kv_part_bytes(B, Hq, Hkv, S, d) == 0
+                   ? nullptr
+                   : reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                              round256((int64_t)B * Hq * T * 8));
+  hipError_t e = attn::launch_backward_bf16(q, k, v, o, lse, dout, dq, dk, dv, bw, B, Hq, Hkv, T,
+                                            S, d, scale, causal != 0,
+                                            static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_EHIP, "attn_bwd: %s", hipGetErrorString(e));
   return ATTN_OK;
 }

@@ -11,7 +11,8 @@
 // grouped-query mapping as attn_fwd).
 //
 // Three kernels, no atomics, so results are bit-reproducible:
-//   bwd_prep_kernel:  D = rowsum(dO * O) per query row (fp32, workspace).
+//   bwd_prep_kernel:  per query row the pair (LSE * log2 e, D = rowsum(dO * O))
+//     in fp32, into the workspace: the row statistics both other kernels read.
 //   bwd_dq_kernel:    one workgroup per 128 query rows of one (batch, head),
 //     shaped like the forward kernel: Q and dO stay in registers as MFMA B
 //     operands, K and V tiles stream through two LDS stages by the
@@ -20,10 +21,12 @@
 //   bwd_dkdv_kernel:  one workgroup per 64 keys of one (batch, KV head); each
 //     wave keeps its 16 keys' K and V in registers as MFMA B operands and
 //     walks every query tile (32 rows) of every query head of the group that
-//     can see them, Q and dO tiles streaming through LDS; per tile S = Q K^T,
-//     dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q with dO and Q
-//     from the transpose read.  Summing the group's heads in registers keeps
-//     the grouped-query reduction exact in order.
+//     can see them.  Q and dO tiles and their rows' statistics stream through
+//     a four-stage LDS ring by the direct-to-LDS load, so three tiles are in
+//     flight while one is computed (a tile is short: 32 MFMAs per wave).  Per
+//     tile S = Q K^T, dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q
+//     with dO and Q from the transpose read.  Summing the group's heads in
+//     registers keeps the grouped-query reduction exact in order.
 // Tiles read both as MFMA row operands and through the transpose read use the
 // dual swizzle of lds_stage.hpp, bank-conflict free for both.
 #include "cdna4.hpp"
@@ -34,11 +37,12 @@ namespace attn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O): 16 lanes per row, D/16 elements per lane.
+// Row statistics (LSE * log2 e, D = rowsum(dO * O)): 16 lanes per row, D/16
+// elements per lane.  stats holds two floats per query row.
 template <int D>
 __global__ __launch_bounds__(256)
 void bwd_prep_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                     float* __restrict__ dsum, long long rows) {
+                     const float* __restrict__ lse, float* __restrict__ stats, long long rows) {
   constexpr int PER = D / 16;
   const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int j = threadIdx.x & 15;
@@ -50,7 +54,7 @@ void bwd_prep_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
   for (int e = 0; e < PER; ++e) acc = __builtin_fmaf((float)op[e], (float)dp[e], acc);
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (j == 0) dsum[row] = acc;
+  if (j == 0) *reinterpret_cast<float2*>(stats + 2 * row) = make_float2(lse[row] * kLog2e, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -61,13 +65,12 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const bf16* __restrict__ v, const bf16* __restrict__ dout,
-                   const float* __restrict__ lse, const float* __restrict__ dsum,
-                   bf16* __restrict__ dq, int B, int Hq, int Hkv, int T, int S,
+                   const float* __restrict__ stats, bf16* __restrict__ dq, int B, int Hq,
+                   int Hkv, int T, int S,
                    float scale_log2, float scale) {
   constexpr int BN = kDqBN;
   constexpr int kBM = 128;
   constexpr int CPR = D / 8;
-  constexpr int NKB = BN / 16;
   constexpr int NDC = D / 32;
   constexpr int NDB = D / 16;
   constexpr int NPC = BN / 32;
@@ -163,8 +166,9 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         qop[qb][c] = *reinterpret_cast<const bf16x8*>(qp + 32 * c);
         dop[qb][c] = *reinterpret_cast<const bf16x8*>(dp + 32 * c);
       }
-      lse2[qb] = lse[(size_t)(b * Hq + h) * T + row] * kLog2e;
-      dd[qb] = dsum[(size_t)(b * Hq + h) * T + row];
+      const float2 st = *reinterpret_cast<const float2*>(stats + 2 * ((size_t)(b * Hq + h) * T + row));
+      lse2[qb] = st.x;
+      dd[qb] = st.y;
     } else {
 #pragma unroll
       for (int c = 0; c < NDC; ++c) qop[qb][c] = dop[qb][c] = bf16x8{};
@@ -186,44 +190,44 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int t_in = 4 * (l16 & 1);
 
   auto compute_tile = [&](int j, const bf16* ks, const bf16* vs) {
-    // S^T[key][row] = K Q^T and dP^T[key][row] = V dO^T
-    f32x4 s[2][NKB], dp[2][NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[0][kb] = s[1][kb] = dp[0][kb] = dp[1][kb] = f32x4{};
-#pragma unroll
-    for (int c = 0; c < NDC; ++c) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const int off = (16 * kb + l16) * D + (((4 * c + g) ^ swz_l) * 8);
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + off);
-        const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vs + off);
-        s[0][kb] = mfma_16x16x32(kop, qop[0][c], s[0][kb]);
-        s[1][kb] = mfma_16x16x32(kop, qop[1][c], s[1][kb]);
-        dp[0][kb] = mfma_16x16x32(vop, dop[0][c], dp[0][kb]);
-        dp[1][kb] = mfma_16x16x32(vop, dop[1][c], dp[1][kb]);
-      }
-    }
-    // dS^T = P^T * (dP^T - D), P^T = exp2(scale_log2 s - LSE2) on visible keys
     const bool need_mask = ((j + 1) * BN > S) || (CAUSAL && (j + 1) * BN - 1 > wrow0 + (S - T));
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float p = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -lse2[qb]));
-          if (need_mask && j * BN + 16 * kb + 4 * g + i > row_lim[qb]) p = 0.f;
-          s[qb][kb][i] = p * (dp[qb][kb][i] - dd[qb]);
-        }
-    // dQ^T[d][row] += K^T[d][key] dS^T[key][row], 32 keys at a time
+    // 32 keys at a time (keeps the score registers to one chunk)
 #pragma unroll
     for (int c = 0; c < NPC; ++c) {
+      // S^T[key][row] = K Q^T and dP^T[key][row] = V dO^T for keys 32 c + 16 kk + ...
+      f32x4 s[2][2], dp[2][2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) s[0][kk] = s[1][kk] = dp[0][kk] = dp[1][kk] = f32x4{};
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int off = (32 * c + 16 * kk + l16) * D + (((4 * dc + g) ^ swz_l) * 8);
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + off);
+          const bf16x8 vop = *reinterpret_cast<const bf16x8*>(vs + off);
+          s[0][kk] = mfma_16x16x32(kop, qop[0][dc], s[0][kk]);
+          s[1][kk] = mfma_16x16x32(kop, qop[1][dc], s[1][kk]);
+          dp[0][kk] = mfma_16x16x32(vop, dop[0][dc], dp[0][kk]);
+          dp[1][kk] = mfma_16x16x32(vop, dop[1][dc], dp[1][kk]);
+        }
+      }
+      // dS^T = P^T * (dP^T - D), P^T = exp2(scale_log2 s - LSE2) on visible keys
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float p = exp2_hw(__builtin_fmaf(s[qb][kk][i], scale_log2, -lse2[qb]));
+            if (need_mask && j * BN + 32 * c + 16 * kk + 4 * g + i > row_lim[qb]) p = 0.f;
+            s[qb][kk][i] = p * (dp[qb][kk][i] - dd[qb]);
+          }
+      // dQ^T[d][row] += K^T[d][key] dS^T[key][row] over these 32 keys
       bf16x8 dsop[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
-        dsop[qb] = pack_bf16x8(s[qb][2 * c][0], s[qb][2 * c][1], s[qb][2 * c][2], s[qb][2 * c][3],
-                               s[qb][2 * c + 1][0], s[qb][2 * c + 1][1], s[qb][2 * c + 1][2],
-                               s[qb][2 * c + 1][3]);
+        dsop[qb] = pack_bf16x8(s[qb][0][0], s[qb][0][1], s[qb][0][2], s[qb][0][3],
+                               s[qb][1][0], s[qb][1][1], s[qb][1][2], s[qb][1][3]);
       const int r0 = 32 * c + t_row, r1 = r0 + 16;
       const int sw0 = dual_swz<D>(r0), sw1 = dual_swz<D>(r1);
 #pragma unroll
@@ -246,6 +250,14 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   };
 
   load_tile(0, k_st0, v_st0);
+  // Settle the register loads above here, outside the loop: a wait the
+  // compiler placed at their first use inside the loop would count the
+  // untracked tile loads issued in between and stall on the next tile.
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(qop[qb][c]), "v"(dop[qb][c]));
+  asm volatile("" ::"v"(lse2[0]), "v"(lse2[1]), "v"(dd[0]), "v"(dd[1]));
   for (int j = 0;;) {
     step(j, k_st0, v_st0, k_st1, v_st1);
     if (++j >= ntk) break;
@@ -270,62 +282,98 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
+// Instruction order for a run of N steps that each take R LDS reads and M
+// MFMAs: the reads of the first two steps, then per step its M MFMAs followed
+// by the reads of the step two ahead.  With one wave per SIMD the only cover
+// for LDS latency is reads in flight; left alone the scheduler pulls each
+// read next to its first use.
+template <int N, int R, int M>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, R * (N < 2 ? N : 2), 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
+    if (i + 2 < N) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// dK, dV.  Workgroup = 4 waves x 16 keys; query tiles of 32 rows.
-constexpr int kKvBK = 64;                    // keys per workgroup
+// dK, dV.  Workgroup = 4 waves x 32 keys (two 16-key blocks per wave), one
+// wave per SIMD: with 32 keys a wave's MFMAs per byte read from LDS double
+// against 16 keys, and the registers that takes (K, V operands and dK, dV
+// accumulators of 32 keys) need the whole register file.  The query heads of
+// a group may be divided between workgroups (head splits) to fill the chip;
+// their fp32 partial dK, dV are then summed in a fixed order by a second kernel.
+constexpr int kKvKeysPerWave = 32;
+constexpr int kKvBK = 4 * kKvKeysPerWave;    // keys per workgroup
 constexpr int kKvBQ = 32;                    // query rows per streamed tile
+constexpr int kKvStages = 4;                 // LDS ring depth
+
+// One ring stage: Q tile, dO tile (both [kKvBQ][D] bf16, dual-swizzled
+// chunks) and the tile rows' statistics ([kKvBQ] x (LSE * log2 e, D)).
+template <int D>
+struct KvStage {
+  static constexpr int kTile = kKvBQ * D * 2;
+  static constexpr int kStats = kKvBQ * 8;
+  static constexpr int kBytes = 2 * kTile + kStats;
+  static constexpr int kRing = kKvStages * kBytes;
+  static constexpr int kCpw = kKvBQ * (D / 8) / 256;   // 16-byte loads per thread per tile
+  static constexpr int kDmaPerStep = 2 * kCpw + 1;      // per wave: Q, dO, statistics
+};
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const bf16* __restrict__ dout,
-                     const float* __restrict__ lse, const float* __restrict__ dsum,
-                     bf16* __restrict__ dk, bf16* __restrict__ dv, int B, int Hq, int Hkv,
-                     int T, int S, float scale_log2, float scale) {
+                     const float* __restrict__ stats, bf16* __restrict__ dk,
+                     bf16* __restrict__ dv, float* __restrict__ part, int B, int Hq, int Hkv,
+                     int T, int S, float scale_log2, float scale, int nsplit) {
+  using L = KvStage<D>;
   constexpr int BQ = kKvBQ;
   constexpr int CPR = D / 8;
   constexpr int NDC = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int CPW = BQ * CPR / 256;        // loads per thread per Q (or dO) tile
+  constexpr int CPW = L::kCpw;
   static_assert(CPW * 256 == BQ * CPR, "tile must split evenly");
+  extern __shared__ __attribute__((aligned(16))) char ring[];
 
-  __shared__ __attribute__((aligned(16))) bf16 q_st0[BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 q_st1[BQ * D];
-  __shared__ __attribute__((aligned(16))) bf16 o_st0[BQ * D];   // dO
-  __shared__ __attribute__((aligned(16))) bf16 o_st1[BQ * D];
-
-  // ---- (key tile, batch, KV head); key tile 0 sees the most rows: first ----
+  // ---- (key tile, batch, KV head, head split); head splits vary fastest so
+  // that the longest causal key tiles (lowest index) start first ----
   const int G = B * Hkv;
-  const int kt = blockIdx.x / G, grp = blockIdx.x % G;
+  const int split = blockIdx.x % nsplit;
+  const int rest = blockIdx.x / nsplit;
+  const int grp = rest % G, kt = rest / G;
   const int b = grp / Hkv, hk = grp % Hkv;
-  const int hpg = Hq / Hkv;
+  const int hpg = Hq / Hkv, hps = hpg / nsplit;
+  const int h_first = hk * hpg + split * hps;
   const int k0 = kt * kKvBK;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int key = k0 + 16 * wave + l16;     // this lane's key (column of S)
-  const bool key_ok = key < S;
+  const int kw0 = k0 + kKvKeysPerWave * wave;  // first key of this wave
   const size_t kvbase = ((size_t)(b * Hkv + hk) * S) * D;
 
   // query tiles that can see some key of this workgroup
   const int ntq = (T + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? max(0, k0 - (S - T)) / BQ : 0;
   const int nq = max(0, ntq - qt0);
-  const int ntiles = nq * hpg;               // (head, q tile) pairs, head-major
+  const int ntiles = nq * hps;               // (head, q tile) pairs, head-major
 
-  // ---- this lane's K and V row as B operands (column key, k-group g) ----
-  bf16x8 kop[NDC], vop[NDC];
-  {
-    const size_t roff = kvbase + (size_t)min(key, S - 1) * D + 8 * g;
+  // ---- K and V rows of this lane's keys kw0 + 16 kb + l16 as B operands ----
+  bf16x8 kop[2][NDC], vop[2][NDC];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const size_t roff = kvbase + (size_t)min(kw0 + 16 * kb + l16, S - 1) * D + 8 * g;
 #pragma unroll
     for (int c = 0; c < NDC; ++c) {
-      kop[c] = *reinterpret_cast<const bf16x8*>(k + roff + 32 * c);
-      vop[c] = *reinterpret_cast<const bf16x8*>(v + roff + 32 * c);
+      kop[kb][c] = *reinterpret_cast<const bf16x8*>(k + roff + 32 * c);
+      vop[kb][c] = *reinterpret_cast<const bf16x8*>(v + roff + 32 * c);
     }
   }
 
-  // ---- direct-to-LDS loads of Q and dO tiles ----
+  // ---- direct-to-LDS loads of one ring stage ----
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   uint32_t toff[CPW];
   int lrow[CPW];
@@ -336,14 +384,21 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     lrow[r] = row;
     toff[r] = (uint32_t)(row * D + (cph ^ dual_swz<D>(row)) * 8) * 2u;
   }
-  auto head_of = [&](int t) { return hk * hpg + t / nq; };
+  const uint32_t ring_lds = lds_addr(ring);
+  auto head_of = [&](int t) { return h_first + t / nq; };
   auto row0_of = [&](int t) { return (qt0 + t % nq) * BQ; };
-  auto load_tile = [&](int t, bf16* qs, bf16* os) {
-    const int h = head_of(t), row0 = row0_of(t);
-    const bf16* qg = q + ((size_t)(b * Hq + h) * T) * D;
-    const bf16* og = dout + ((size_t)(b * Hq + h) * T) * D;
-    const uint32_t ql = lds_addr(qs) + (uint32_t)(wave_s * CPW) * 1024u;
-    const uint32_t ol = lds_addr(os) + (uint32_t)(wave_s * CPW) * 1024u;
+  // Tile t into stage t % kKvStages.  Past the last tile the last tile is
+  // loaded again (into a stage nobody reads), which keeps the number of loads
+  // per step, and so the wait counts below, the same on every step.
+  auto issue = [&](int t) {
+    const int tc = min(t, ntiles - 1);
+    const int h = head_of(tc), row0 = row0_of(tc);
+    const size_t hbase = (size_t)(b * Hq + h) * T;
+    const bf16* qg = q + hbase * D;
+    const bf16* og = dout + hbase * D;
+    const uint32_t sb = ring_lds + (uint32_t)((t % kKvStages) * L::kBytes);
+    const uint32_t ql = sb + (uint32_t)(wave_s * CPW) * 1024u;
+    const uint32_t ol = ql + (uint32_t)L::kTile;
     const bool full = row0 + BQ <= T;
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
@@ -352,155 +407,269 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       lds_dma16(qg, toff[r] + add, ql + 1024u * r);
       lds_dma16(og, toff[r] + add, ol + 1024u * r);
     }
-  };
-  // LSE (log2 units) and D of rows row0 + 16 qb + 4 g + i (rows past T: 0)
-  auto load_stats = [&](int t, f32x4 (&ls)[2], f32x4 (&ds)[2]) {
-    const size_t base = (size_t)(b * Hq + head_of(t)) * T;
-    const int row0 = row0_of(t);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = min(row0 + 16 * qb + 4 * g + i, T - 1);
-        ls[qb][i] = lse[base + row] * kLog2e;
-        ds[qb][i] = dsum[base + row];
-      }
+    // statistics of rows row0 + 8 wave .. + 7: 16 dwords from this wave
+    if (lane < 16) {
+      const int row = min(row0 + 8 * wave + (lane >> 1), T - 1);
+      lds_dma4(stats + 2 * hbase, (uint32_t)(row * 8 + (lane & 1) * 4),
+               sb + (uint32_t)(2 * L::kTile + 64 * wave_s));
+    }
   };
 
-  f32x4 dka[NDB], dva[NDB];                  // dK[key][d], dV[key][d] (rows key, cols d)
+  f32x4 dka[2][NDB], dva[2][NDB];            // dK[key][d], dV[key][d] per 16-key block
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dka[db] = dva[db] = f32x4{};
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) dka[kb][db] = dva[kb][db] = f32x4{};
 
   const int t_row = 4 * g + (l16 >> 2);
   const int t_chunk = (l16 & 3) >> 1;
   const int t_in = 4 * (l16 & 1);
   const int sw_lo = dual_swz<D>(t_row), sw_hi = dual_swz<D>(t_row + 16);
   const int swz_l = dual_swz<D>(l16);
+  const bool edge_keys = k0 + kKvBK > S;     // some key of the workgroup is past S
 
-  auto compute_tile = [&](int t, const bf16* qs, const bf16* os, const f32x4 (&ls)[2],
-                          const f32x4 (&dsv)[2]) {
+  auto compute_tile = [&](int t) {
+    const char* sp = ring + (t % kKvStages) * L::kBytes;
+    const bf16* qs = reinterpret_cast<const bf16*>(sp);
+    const bf16* os = reinterpret_cast<const bf16*>(sp + L::kTile);
+    const float4* st = reinterpret_cast<const float4*>(sp + 2 * L::kTile);
     const int row0 = row0_of(t);
     // S[row][key] = Q K^T and dP[row][key] = dO V^T (rows 16 qb + 4 g + i, column key)
-    f32x4 s[2], dp[2];
-    s[0] = s[1] = dp[0] = dp[1] = f32x4{};
+    f32x4 s[2][2], dp[2][2];
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
+    for (int qb = 0; qb < 2; ++qb) s[qb][0] = s[qb][1] = dp[qb][0] = dp[qb][1] = f32x4{};
+    // all operand reads first: one wave per SIMD hides LDS latency only by
+    // having many reads in flight
+    bf16x8 qa[NDC][2], oa[NDC][2];
+#pragma unroll
+    for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         const int off = (16 * qb + l16) * D + (((4 * c + g) ^ swz_l) * 8);
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qs + off);
-        const bf16x8 oa = *reinterpret_cast<const bf16x8*>(os + off);
-        s[qb] = mfma_16x16x32(qa, kop[c], s[qb]);
-        dp[qb] = mfma_16x16x32(oa, vop[c], dp[qb]);
+        qa[c][qb] = *reinterpret_cast<const bf16x8*>(qs + off);
+        oa[c][qb] = *reinterpret_cast<const bf16x8*>(os + off);
+      }
+#pragma unroll
+    for (int c = 0; c < NDC; ++c)
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          s[qb][kb] = mfma_16x16x32(qa[c][qb], kop[kb][c], s[qb][kb]);
+          dp[qb][kb] = mfma_16x16x32(oa[c][qb], vop[kb][c], dp[qb][kb]);
+        }
+    // keep the reads of two d-chunks ahead of the MFMAs that use them
+    sched_reads_ahead<NDC, 4, 8>();
+    // P = exp2(scale_log2 s - LSE2) and dS = P (dP - D), zero off the visible pairs
+    float pv[2][2][4], dsw[2][2][4];         // [kb][qb][i]
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      // (LSE * log2 e, D) of rows 16 qb + 4 g + 0..3
+      const float4 ab = st[8 * qb + 2 * g], cd = st[8 * qb + 2 * g + 1];
+      const float lse2[4] = {ab.x, ab.z, cd.x, cd.z};
+      const float dd[4] = {ab.y, ab.w, cd.y, cd.w};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[kb][qb][i] = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -lse2[i]));
+          dsw[kb][qb][i] = dp[qb][kb][i] - dd[i];
+        }
+    }
+    if (edge_keys || row0 + BQ > T || (CAUSAL && k0 + kKvBK - 1 > row0 + (S - T))) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kw0 + 16 * kb + l16;
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = row0 + 16 * qb + 4 * g + i;
+            const bool hide = key >= S || row >= T || (CAUSAL && key > row + (S - T));
+            pv[kb][qb][i] = hide ? 0.f : pv[kb][qb][i];
+          }
       }
     }
-    // P and dS on visible (row, key) pairs
-    const bool need_mask = !key_ok || row0 + BQ > T || (CAUSAL && k0 + kKvBK - 1 > row0 + (S - T));
-    float pv[2][4], dsw[2][4];
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = row0 + 16 * qb + 4 * g + i;
-        float p = exp2_hw(__builtin_fmaf(s[qb][i], scale_log2, -ls[qb][i]));
-        if (need_mask && (!key_ok || row >= T || (CAUSAL && key > row + (S - T)))) p = 0.f;
-        pv[qb][i] = p;
-        dsw[qb][i] = p * (dp[qb][i] - dsv[qb][i]);
-      }
     // A operands: row = this lane's key, k-slots = rows 4g..4g+3 then 16+4g..16+4g+3
-    const bf16x8 pta = pack_bf16x8(pv[0][0], pv[0][1], pv[0][2], pv[0][3],
-                                   pv[1][0], pv[1][1], pv[1][2], pv[1][3]);
-    const bf16x8 dsta = pack_bf16x8(dsw[0][0], dsw[0][1], dsw[0][2], dsw[0][3],
-                                    dsw[1][0], dsw[1][1], dsw[1][2], dsw[1][3]);
+    bf16x8 pta[2], dsta[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      pta[kb] = pack_bf16x8(pv[kb][0][0], pv[kb][0][1], pv[kb][0][2], pv[kb][0][3],
+                            pv[kb][1][0], pv[kb][1][1], pv[kb][1][2], pv[kb][1][3]);
+      dsta[kb] = pack_bf16x8(pv[kb][0][0] * dsw[kb][0][0], pv[kb][0][1] * dsw[kb][0][1],
+                             pv[kb][0][2] * dsw[kb][0][2], pv[kb][0][3] * dsw[kb][0][3],
+                             pv[kb][1][0] * dsw[kb][1][0], pv[kb][1][1] * dsw[kb][1][1],
+                             pv[kb][1][2] * dsw[kb][1][2], pv[kb][1][3] * dsw[kb][1][3]);
+    }
     // dV += P^T dO and dK += dS^T Q, the B operands from the transpose read
+    bf16x8 ob[NDB], qbo[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int ch = 2 * db + t_chunk;
       const int off_lo = t_row * D + t_in + (ch ^ sw_lo) * 8;
       const int off_hi = (t_row + 16) * D + t_in + (ch ^ sw_hi) * 8;
-      const bf16x8 ob = concat_tr(lds_read_tr16(os + off_lo), lds_read_tr16(os + off_hi));
-      const bf16x8 qbop = concat_tr(lds_read_tr16(qs + off_lo), lds_read_tr16(qs + off_hi));
-      dva[db] = mfma_16x16x32(pta, ob, dva[db]);
-      dka[db] = mfma_16x16x32(dsta, qbop, dka[db]);
+      ob[db] = concat_tr(lds_read_tr16(os + off_lo), lds_read_tr16(os + off_hi));
+      qbo[db] = concat_tr(lds_read_tr16(qs + off_lo), lds_read_tr16(qs + off_hi));
     }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dva[kb][db] = mfma_16x16x32(pta[kb], ob[db], dva[kb][db]);
+        dka[kb][db] = mfma_16x16x32(dsta[kb], qbo[db], dka[kb][db]);
+      }
+    sched_reads_ahead<NDB, 4, 4>();
   };
 
   if (ntiles > 0) {
-    f32x4 lsa[2], dsa[2], lsb[2], dsb[2];
-    load_tile(0, q_st0, o_st0);
-    load_stats(0, lsa, dsa);
-    auto step = [&](int t, const bf16* qs, const bf16* os, bf16* qn, bf16* on, const f32x4 (&ls)[2],
-                    const f32x4 (&dsv)[2], f32x4 (&lsn)[2], f32x4 (&dsn)[2]) {
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));
+#pragma unroll
+    for (int t = 0; t < kKvStages - 1; ++t) issue(t);
+    // K and V register loads settle here, not at a first use inside the loop
+    // (see the dQ kernel)
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(kop[kb][c]), "v"(vop[kb][c]));
+    for (int t = 0; t < ntiles; ++t) {
+      // this wave's loads of tile t are done once at most the two later
+      // tiles' loads are outstanding; the barrier then publishes every wave's
+      // part and frees the stage of tile t - 1 for tile t + 3
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits((kKvStages - 2) * L::kDmaPerStep));
       stage_barrier();
-      if (t + 1 < ntiles) {
-        load_tile(t + 1, qn, on);
-        load_stats(t + 1, lsn, dsn);
-      }
-      compute_tile(t, qs, os, ls, dsv);
-    };
-    for (int t = 0;;) {
-      step(t, q_st0, o_st0, q_st1, o_st1, lsa, dsa, lsb, dsb);
-      if (++t >= ntiles) break;
-      step(t, q_st1, o_st1, q_st0, o_st0, lsb, dsb, lsa, dsa);
-      if (++t >= ntiles) break;
+      issue(t + kKvStages - 1);
+      compute_tile(t);
     }
+    // the re-loads past the last tile land before the workgroup's LDS is released
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));
   }
 
-  // ---- dK = scale * dK, dV: rows key 4 g + i of the wave's 16, columns d ----
+  // ---- rows key 16 kb + 4 g + i of the wave's 32, columns 16 db + l16 ----
+  if (nsplit == 1) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int kr = k0 + 16 * wave + 4 * g + i;
-    if (kr < S) {
-      bf16* kp = dk + kvbase + (size_t)kr * D + l16;
-      bf16* vp = dv + kvbase + (size_t)kr * D + l16;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        kp[16 * db] = (bf16)(dka[db][i] * scale);
-        vp[16 * db] = (bf16)dva[db][i];
+      for (int i = 0; i < 4; ++i) {
+        const int kr = kw0 + 16 * kb + 4 * g + i;
+        if (kr < S) {
+          bf16* kp = dk + kvbase + (size_t)kr * D + l16;
+          bf16* vp = dv + kvbase + (size_t)kr * D + l16;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            kp[16 * db] = (bf16)(dka[kb][db][i] * scale);
+            vp[16 * db] = (bf16)dva[kb][db][i];
+          }
+        }
       }
-    }
+  } else {
+    // fp32 partials of this head split: part[split][0: dK, 1: dV][B*Hkv*S*D]
+    const size_t nkv = (size_t)B * Hkv * S * D;
+    float* pk = part + (size_t)(2 * split) * nkv + kvbase;
+    float* pvv = pk + nkv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int kr = kw0 + 16 * kb + 4 * g + i;
+        if (kr < S) {
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            pk[(size_t)kr * D + 16 * db + l16] = dka[kb][db][i];
+            pvv[(size_t)kr * D + 16 * db + l16] = dva[kb][db][i];
+          }
+        }
+      }
   }
+}
+
+// dK = scale * sum over head splits, dV = sum, in split order; 4 elements per thread.
+__global__ __launch_bounds__(256)
+void bwd_kv_reduce_kernel(const float* __restrict__ part, bf16* __restrict__ dk,
+                          bf16* __restrict__ dv, long long nkv, int nsplit, float scale) {
+  const long long e = ((long long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= nkv) return;                      // nkv is a multiple of 64
+  float4 ak = *reinterpret_cast<const float4*>(part + e);
+  float4 av = *reinterpret_cast<const float4*>(part + nkv + e);
+  for (int sp = 1; sp < nsplit; ++sp) {
+    const float4 bk = *reinterpret_cast<const float4*>(part + (size_t)(2 * sp) * nkv + e);
+    const float4 bv = *reinterpret_cast<const float4*>(part + (size_t)(2 * sp + 1) * nkv + e);
+    ak.x += bk.x; ak.y += bk.y; ak.z += bk.z; ak.w += bk.w;
+    av.x += bv.x; av.y += bv.y; av.z += bv.z; av.w += bv.w;
+  }
+  bf16x4 rk, rv;
+  rk[0] = (bf16)(ak.x * scale); rk[1] = (bf16)(ak.y * scale);
+  rk[2] = (bf16)(ak.z * scale); rk[3] = (bf16)(ak.w * scale);
+  rv[0] = (bf16)av.x; rv[1] = (bf16)av.y; rv[2] = (bf16)av.z; rv[3] = (bf16)av.w;
+  *reinterpret_cast<bf16x4*>(dk + e) = rk;
+  *reinterpret_cast<bf16x4*>(dv + e) = rv;
 }
 
 template <int D, bool CAUSAL>
 hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                        float* dsum, int B, int Hq, int Hkv, int T, int S, float scale,
+                        const BwdWorkspace& ws, int B, int Hq, int Hkv, int T, int S, float scale,
                         hipStream_t stream) {
   const long long rows = (long long)B * Hq * T;
   hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     static_cast<const bf16*>(o), static_cast<const bf16*>(dout), dsum, rows);
+                     static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, ws.stats, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * kLog2e;
   const long long gq = (long long)((T + 127) / 128) * B * Hq;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, dsum,
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
                      static_cast<bf16*>(dq), B, Hq, Hkv, T, S, scale_log2, scale);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const long long gkv = (long long)((S + kKvBK - 1) / kKvBK) * B * Hkv;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gkv), dim3(256), 0, stream,
+  // the ring is above the 64 KB of static LDS at d = 128
+  e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, KvStage<D>::kRing);
+  if (e != hipSuccess) return e;
+  const int nsplit = bwd_kv_splits(B, Hq, Hkv, S);
+  const long long gkv = (long long)((S + kKvBK - 1) / kKvBK) * B * Hkv * nsplit;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gkv), dim3(256),
+                     KvStage<D>::kRing, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), lse, dsum,
-                     static_cast<bf16*>(dk), static_cast<bf16*>(dv), B, Hq, Hkv, T, S, scale_log2,
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
+                     static_cast<bf16*>(dk), static_cast<bf16*>(dv), ws.kv_part, B, Hq, Hkv, T, S,
+                     scale_log2, scale, nsplit);
+  e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const long long nkv = (long long)B * Hkv * S * D;
+  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((nkv / 4 + 255) / 256)), dim3(256), 0,
+                     stream, ws.kv_part, static_cast<bf16*>(dk), static_cast<bf16*>(dv), nkv, nsplit,
                      scale);
   return hipGetLastError();
 }
 
 }  // namespace
 
+int bwd_kv_splits(int B, int Hq, int Hkv, int S) {
+  const long long base = (long long)((S + kKvBK - 1) / kKvBK) * B * Hkv;
+  const int hpg = Hq / Hkv;
+  int n = 1;
+  while (base * n < kBwdTargetBlocks && n < hpg) {
+    int m = n + 1;
+    while (hpg % m != 0) ++m;
+    n = m;
+  }
+  return n;
+}
+
+size_t bwd_kv_part_bytes(int B, int Hq, int Hkv, int S, int d) {
+  const int n = bwd_kv_splits(B, Hq, Hkv, S);
+  return n == 1 ? 0 : (size_t)2 * n * B * Hkv * S * d * 4;
+}
+
 hipError_t launch_backward_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                float* dsum, int B, int Hq, int Hkv, int T, int S, int d,
-                                float scale, bool causal, hipStream_t stream) {
+                                const BwdWorkspace& ws, int B, int Hq, int Hkv, int T, int S,
+                                int d, float scale, bool causal, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_bwd_d<128, true>(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, T, S, scale, stream)
-                  : launch_bwd_d<128, false>(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, T, S, scale, stream);
-  return causal ? launch_bwd_d<64, true>(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, T, S, scale, stream)
-                : launch_bwd_d<64, false>(q, k, v, o, lse, dout, dq, dk, dv, dsum, B, Hq, Hkv, T, S, scale, stream);
+    return causal ? launch_bwd_d<128, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, scale, stream)
+                  : launch_bwd_d<128, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, scale, stream);
+  return causal ? launch_bwd_d<64, true>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, scale, stream)
+                : launch_bwd_d<64, false>(q, k, v, o, lse, dout, dq, dk, dv, ws, B, Hq, Hkv, T, S, scale, stream);
 }
 
 }  // namespace attn

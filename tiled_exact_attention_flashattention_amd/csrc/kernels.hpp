@@ -37,11 +37,26 @@ hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
                                float scale_log2, hipStream_t stream);
 
-// Backward, bf16 in/out, fp32 accumulation on MFMA: D = rowsum(dO * O) into
-// `dsum` [B*Hq*T] floats, then dQ, then dK and dV (three launches, no atomics).
+// Backward, bf16 in/out, fp32 accumulation on MFMA: the row statistics
+// (LSE * log2 e, D = rowsum(dO * O)) into ws.stats [B*Hq*T][2] floats, then
+// dQ, then dK and dV; when the query heads of a group are divided between
+// workgroups (bwd_kv_splits > 1), their fp32 partials go to ws.kv_part
+// [splits][2][B*Hkv*S*d] and a last kernel sums them.  No atomics.
+constexpr int kBwdTargetBlocks = 512;   // dK/dV workgroups wanted: two rounds of 256 CUs
+
+struct BwdWorkspace {
+  float* stats;
+  float* kv_part;                      // null when bwd_kv_splits(...) == 1
+};
+
+// Head splits of the dK/dV kernel for these sizes: the smallest divisor n of
+// Hq / Hkv with ceil(S / 128) * B * Hkv * n >= kBwdTargetBlocks (else Hq / Hkv).
+int bwd_kv_splits(int B, int Hq, int Hkv, int S);
+size_t bwd_kv_part_bytes(int B, int Hq, int Hkv, int S, int d);
+
 hipError_t launch_backward_bf16(const void* q, const void* k, const void* v, const void* o,
                                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                                float* dsum, int B, int Hq, int Hkv, int T, int S, int d,
-                                float scale, bool causal, hipStream_t stream);
+                                const BwdWorkspace& ws, int B, int Hq, int Hkv, int T, int S,
+                                int d, float scale, bool causal, hipStream_t stream);
 
 }  // namespace attn

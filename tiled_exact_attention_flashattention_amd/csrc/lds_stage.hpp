@@ -29,6 +29,13 @@ __device__ __forceinline__ void lds_dma16(const void* sbase, uint32_t voff, uint
                :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
+// The 4-byte form: lane i's dword from `sbase` + `voff` lands at `lds_base` +
+// 4 i.  Lanes switched off by the execution mask load nothing.
+__device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
