@@ -391,14 +391,14 @@ def test_unmodified_oracle_passes_the_pin_set():
     assert _pins_pass()
 
 
-def _mask_off_by_one(rows, S, T, causal):
+def _mask_off_by_one(rows, S, T, causal, window=0):
     rows = np.asarray(rows)
     if not causal:
         return np.ones((rows.shape[0], S), dtype=bool)
     return np.arange(S)[None, :] < (rows[:, None] + (S - T))
 
 
-def _mask_top_left(rows, S, T, causal):
+def _mask_top_left(rows, S, T, causal, window=0):
     rows = np.asarray(rows)
     if not causal:
         return np.ones((rows.shape[0], S), dtype=bool)
