@@ -20,6 +20,8 @@ Reported (one JSON line on stdout):
                  kernel sources still match the recorded hash, else null;
   prefill_other  the same causal prefill timing on the two larger prefill
                  workloads (GQA B=4 T=4096 d=128; long B=1 H=32 T=16384 d=128);
+  window         attn_fwd_window on the GQA causal workload with a 1024-key
+                 sliding window (FLOPs over the visible pairs only);
   backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
                  kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
                  T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
@@ -67,9 +69,9 @@ def sources_sha(kind):
     return h.hexdigest()[:16]
 
 
-def prefill_work(B, Hq, Hkv, T, S, d, causal, elem):
+def prefill_work(B, Hq, Hkv, T, S, d, causal, elem, window=0):
     if causal:
-        pairs = sum(min(S, i + (S - T) + 1) for i in range(T))
+        pairs = sum(min(S, i + (S - T) + 1, window if window else S) for i in range(T))
     else:
         pairs = T * S
     flops = 4 * d * pairs * B * Hq
@@ -135,6 +137,40 @@ def cpu_baseline(pinp, dinp, budget_s):
         "decode_value": dbytes / td / 1e9, "decode_unit": "GB/s",
         "host_cpus": len(os.sched_getaffinity(0)),
     }
+
+
+def timed_launches(stream, flush, launch, n=7, skip=2):
+    """Mean HIP-event time (ms) of launch() over n cold launches, the first `skip` untimed."""
+    import torch
+    times = []
+    for i in range(n):
+        if flush is not None:
+            flush.sum()
+        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        launch()
+        b_.record(stream)
+        if i >= skip:
+            times.append((a, b_))
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b_) for a, b_ in times) / len(times), len(times)
+
+
+def bench_window(tea, workloads, dev, stream, flush, window=1024):
+    """attn_fwd_window on the GQA causal workload."""
+    import torch
+    x = workloads.prefill_3()
+    xq, xk, xv = (t.to(dev) for t in (x.q, x.k, x.v))
+    xo = torch.empty_like(xq)
+    xl = torch.empty((x.B, x.Hq, x.T), dtype=torch.float32, device=dev)
+    ms, n = timed_launches(stream, flush, lambda: tea.attn_fwd_window(
+        xq, xk, xv, xo, xl, x.scale, window, stream=stream))
+    fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, True, 2, window=window)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal, "
+                      f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms, "value": tf,
+            "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
+            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
 
 
 def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
@@ -262,6 +298,8 @@ def main():
     ap.add_argument("--no-other-prefill", action="store_true",
                     help="skip the timing of the two larger prefill workloads")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the sliding-window, chunked-prefill and fp8-decode timings")
     args = ap.parse_args()
     if args.write_counters:
         write_counters(args.write_counters)
@@ -411,6 +449,8 @@ def main():
                            "launches": len(times)}
             del xq, xk, xv, xo, xl
         out["prefill_other"] = other
+    if not args.no_next:
+        out["window"] = bench_window(tea, workloads, dev, stream, flush)
     if not args.no_backward:
         out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
                                          None if args.no_cpu_baseline else args.cpu_budget / 3)

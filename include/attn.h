@@ -1,12 +1,13 @@
 /*
  * attn.h -- C ABI of the MI355X (gfx950) tiled exact attention library.
  *
- * Three operations, each computing exactly softmax(scale * Q K^T) V, or its
+ * Operations, each computing exactly softmax(scale * Q K^T) V, or its
  * gradients, without the score matrix ever reaching device memory:
  *
  *   attn_fwd           prefill: every query row of a sequence against its keys,
  *                      optionally causal, with grouped-query heads, writing O
  *                      and the per-row log-sum-exp.
+ *   attn_fwd_window    the same, causal, limited to a sliding window of keys.
  *   attn_bwd           the gradients dQ, dK, dV of attn_fwd's output for a
  *                      given output gradient dO, rebuilding the probabilities
  *                      tile by tile from the saved log-sum-exp.
@@ -95,6 +96,23 @@ typedef enum {
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal,
              int dtype, void* stream);
+
+/*
+ * attn_fwd_window -- causal prefill with a sliding window.
+ *
+ * As attn_fwd with causal = 1, except that query i also loses every key
+ * j <= i + (S - T) - window: it sees its own position and the window - 1
+ * before it.  "Advanced Attention Mechanisms - II" (A. Das), section "Flash
+ * Attention", names sliding-window attention among the methods that cut
+ * memory and compute; this window rule is our reading of that name.  Key
+ * tiles wholly outside a query tile's window are skipped, not masked.
+ *
+ * Requirements: as for attn_fwd (causal); window >= 1 (else ATTN_EINVAL).
+ * window >= S gives exactly attn_fwd's causal result.
+ */
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int T, int S, int d, float scale, int window,
+                    int dtype, void* stream);
 
 /*
  * attn_bwd -- gradients of attn_fwd.

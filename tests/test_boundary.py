@@ -26,8 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
-                                     "attn_decode_workspace_size", "attn_fwd", "attn_last_error",
-                                     "attn_status_string"]
+                                     "attn_decode_workspace_size", "attn_fwd", "attn_fwd_window",
+                                     "attn_last_error", "attn_status_string"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -111,6 +111,25 @@ def test_fwd_f32_shares_the_checks():
 def test_fwd_rejects_heads_past_32_bit_offsets():
     assert _fwd(T=1 << 24, S=1 << 24, d=128, B=1, Hq=1, Hkv=1, causal=0) == ATTN_EINVAL
     assert "2^31" in tea.attn_last_error()
+
+
+def _fwd_window(window, **kw):
+    a = dict(FWD_OK)
+    a.update(kw)
+    return tea.lib().attn_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                                     a["Hkv"], a["T"], a["S"], a["d"], a["scale"], window,
+                                     a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("window,bad,code", [
+    (0, {}, ATTN_EINVAL), (-5, {}, ATTN_EINVAL),
+    (16, dict(T=65, S=64), ATTN_EINVAL),          # causal needs T <= S
+    (16, dict(q=None), ATTN_EINVAL), (16, dict(d=96), ATTN_EUNSUPPORTED),
+    (16, dict(scale=float("nan")), ATTN_EINVAL), (16, dict(o=P), ATTN_EINVAL),
+])
+def test_fwd_window_rejects_bad_arguments(window, bad, code):
+    assert _fwd_window(window, **bad) == code
+    assert tea.attn_last_error().startswith("attn_fwd_window")
 
 
 # --- attn_bwd argument checks ---------------------------------------------------

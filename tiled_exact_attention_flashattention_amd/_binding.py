@@ -74,6 +74,9 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32,
                                     f32, i32, vp, sz, vp]
     L.attn_decode_paged.restype = i32
+    L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
+                                  vp]
+    L.attn_fwd_window.restype = i32
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                            i32, i32, vp, sz, vp]
     L.attn_bwd.restype = i32
@@ -163,6 +166,25 @@ def attn_fwd(q, k, v, o, lse, scale: float, causal: bool, stream=None) -> None:
     _check(st)
 
 
+def attn_fwd_window(q, k, v, o, lse, scale: float, window: int, stream=None) -> None:
+    """Enqueue attn_fwd_window (causal, sliding window of ``window`` keys)."""
+    import torch
+    _require_device_tensors(q, k, v, o, lse)
+    B, Hq, T, d = q.shape
+    Hkv, S = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, S, d) or v.shape != k.shape or o.shape != q.shape:
+        raise ValueError("shape mismatch among q, k, v, o")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise TypeError("q, k, v, o must share one dtype")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (B, Hq, T)):
+        raise ValueError("lse must be float32 [B, Hq, T]")
+    st = lib().attn_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr() if lse is not None else None,
+                               B, Hq, Hkv, T, S, d, float(scale), int(window), _dtype_code(q),
+                               _stream_ptr(q.device, stream))
+    _check(st)
+
+
 def attn_bwd(q, k, v, o, lse, dout, dq, dk, dv, scale: float, causal: bool, workspace,
              stream=None) -> None:
     """Enqueue attn_bwd on ``stream`` (default: the current stream of q's device).
@@ -223,14 +245,19 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: f
 
 # ---- conveniences that allocate outputs with torch ---------------------------
 
-def fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, with_lse: bool = True):
-    """Allocate O (and LSE) and run attn_fwd.  Returns (o, lse)."""
+def fwd(q, k, v, scale: Optional[float] = None, causal: bool = False, with_lse: bool = True,
+        window: int = 0):
+    """Allocate O (and LSE) and run attn_fwd (attn_fwd_window if window > 0,
+    which implies causal).  Returns (o, lse)."""
     import torch
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if with_lse else None
-    attn_fwd(q, k, v, o, lse, scale, causal)
+    if window:
+        attn_fwd_window(q, k, v, o, lse, scale, window)
+    else:
+        attn_fwd(q, k, v, o, lse, scale, causal)
     return o, lse
 
 

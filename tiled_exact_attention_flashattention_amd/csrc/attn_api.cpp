@@ -89,45 +89,70 @@ size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page
   return decode_workspace_layout(N, Hq, d).total;
 }
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
-             int Hkv, int T, int S, int d, float scale, int causal, int dtype, void* stream) {
-  if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "attn_fwd: q, k, v and o must be non-NULL");
+}  // extern "C"
+
+namespace {
+
+// attn_fwd and attn_fwd_window: `fn` names the entry point in messages.
+int fwd_common(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal, int window,
+               int dtype, void* stream) {
+  if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1)
-    return fail(ATTN_EINVAL, "attn_fwd: sizes must be >= 1 (B=%d Hq=%d Hkv=%d T=%d S=%d d=%d)", B,
+    return fail(ATTN_EINVAL, "%s: sizes must be >= 1 (B=%d Hq=%d Hkv=%d T=%d S=%d d=%d)", fn, B,
                 Hq, Hkv, T, S, d);
-  if (Hq % Hkv != 0) return fail(ATTN_EINVAL, "attn_fwd: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+  if (Hq % Hkv != 0) return fail(ATTN_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (causal && T > S)
-    return fail(ATTN_EINVAL, "attn_fwd: causal attention needs T <= S (T=%d S=%d)", T, S);
+    return fail(ATTN_EINVAL, "%s: causal attention needs T <= S (T=%d S=%d)", fn, T, S);
+  if (window < 0) return fail(ATTN_EINVAL, "%s: window must be >= 1", fn);
   if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(ATTN_EINVAL, "attn_fwd: scale must be finite and > 0");
+    return fail(ATTN_EINVAL, "%s: scale must be finite and > 0", fn);
   if (dtype != ATTN_F32 && dtype != ATTN_BF16)
-    return fail(ATTN_EUNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
-  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "attn_fwd: head dim %d (need 64 or 128)", d);
+    return fail(ATTN_EUNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "%s: head dim %d (need 64 or 128)", fn, d);
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) ||
       (lse && !aligned(lse, 4)))
-    return fail(ATTN_EINVAL, "attn_fwd: q/k/v/o need 16-byte alignment, lse 4-byte");
+    return fail(ATTN_EINVAL, "%s: q/k/v/o need 16-byte alignment, lse 4-byte", fn);
   const int64_t qn = (int64_t)B * Hq * T * d, kn = (int64_t)B * Hkv * S * d;
-  if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "attn_fwd: tensor too large");
+  if (qn > kMaxElems || kn > kMaxElems) return fail(ATTN_EINVAL, "%s: tensor too large", fn);
   if ((int64_t)T * d >= kMaxHeadElems || (int64_t)S * d >= kMaxHeadElems)
-    return fail(ATTN_EINVAL, "attn_fwd: T*d and S*d must be below 2^31");
+    return fail(ATTN_EINVAL, "%s: T*d and S*d must be below 2^31", fn);
   const int64_t grid = ((int64_t)T + 127) / 128 * B * Hq;
-  if (grid > 0x7fffffff) return fail(ATTN_EINVAL, "attn_fwd: too many query tiles");
+  if (grid > 0x7fffffff) return fail(ATTN_EINVAL, "%s: too many query tiles", fn);
   const size_t es = dtype == ATTN_BF16 ? 2 : 4;
   const size_t qb = qn * es, kb = kn * es, lb = lse ? (size_t)B * Hq * T * 4 : 0;
   if (overlap(o, qb, q, qb) || overlap(o, qb, k, kb) || overlap(o, qb, v, kb) ||
       overlap(lse, lb, q, qb) || overlap(lse, lb, k, kb) || overlap(lse, lb, v, kb) ||
       overlap(lse, lb, o, qb))
-    return fail(ATTN_EINVAL, "attn_fwd: o/lse overlap an input or each other");
+    return fail(ATTN_EINVAL, "%s: o/lse overlap an input or each other", fn);
 
   const float scale_log2 = scale * kLog2e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e = dtype == ATTN_BF16
                      ? attn::launch_prefill_bf16(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale_log2,
-                                                 causal != 0, st)
+                                                 causal != 0, window, st)
                      : attn::launch_prefill_f32(q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale_log2,
-                                                causal != 0, st);
-  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_fwd: %s", hipGetErrorString(e));
+                                                causal != 0, window, st);
+  if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq,
+             int Hkv, int T, int S, int d, float scale, int causal, int dtype, void* stream) {
+  return fwd_common("attn_fwd", q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, causal, 0, dtype,
+                    stream);
+}
+
+int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int Hq, int Hkv, int T, int S, int d, float scale, int window, int dtype,
+                    void* stream) {
+  if (window < 1) return fail(ATTN_EINVAL, "attn_fwd_window: window must be >= 1 (got %d)", window);
+  return fwd_common("attn_fwd_window", q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, 1, window,
+                    dtype, stream);
 }
 
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -10,14 +10,15 @@
 namespace attn {
 
 // Prefill, bf16 in/out, fp32 accumulation on MFMA.  scale_log2 = scale*log2(e).
+// window > 0 (causal only): sliding window of that many keys; 0: none.
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int Hq, int Hkv, int T, int S, int d,
-                               float scale_log2, bool causal, hipStream_t stream);
+                               float scale_log2, bool causal, int window, hipStream_t stream);
 
 // Prefill, fp32 in/out, fp32 arithmetic on the vector ALUs.
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int Hq, int Hkv, int T, int S, int d,
-                              float scale_log2, bool causal, hipStream_t stream);
+                              float scale_log2, bool causal, int window, hipStream_t stream);
 
 // Paged decode: a persistent grid of kDecodeWaves single-wave workgroups that
 // split all page pairs evenly, then a combine kernel for the sequences they

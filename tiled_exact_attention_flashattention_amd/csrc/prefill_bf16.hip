@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_wa
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
-                         float scale_log2) {
+                         float scale_log2, int window) {
   constexpr int BN = PrefillCfg<D>::BN;
   constexpr int NST = PrefillCfg<D>::STAGES;
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
@@ -146,6 +146,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     wave_kv_end = min(S, min(wrow0 + kWR, T) + (S - T));
   }
   const int ntk = (wg_kv_end + BN - 1) / BN;
+  // Causal sliding window: row i also loses keys <= i + (S - T) - window.
+  // Tiles wholly left of the first row's window are never loaded (j0), and a
+  // wave skips those left of its own first row's window.
+  const bool windowed = CAUSAL && window > 0;
+  const int wave_kv_lo = windowed ? max(0, wrow0 + (S - T) - window + 1) : 0;
+  const int j0 = windowed ? max(0, q0 + (S - T) - window + 1) / BN : 0;
 
   // ---- direct-to-LDS tile load ----
   // Instruction r of wave w fills LDS chunks [64 (w CPW + r), +64): lane l
@@ -188,7 +194,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- Q rows into registers (B operand of S^T = K Q^T) ----
   bf16x8 qop[QB][NDC];
-  int row_lim[QB];
+  int row_lim[QB], row_lo[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = wrow0 + 16 * qb + l16;
@@ -202,6 +208,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     // last key visible to this row (rows past T only feed discarded lanes)
     row_lim[qb] = CAUSAL ? min(row + (S - T), S - 1) : S - 1;
+    row_lo[qb] = windowed ? row + (S - T) - window + 1 : 0;
   }
 
   // ---- running softmax state of rows wrow0 + 16 qb + l16 ----
@@ -253,6 +260,18 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           for (int i = 0; i < 4; ++i) {
             const int key = j * BN + 16 * kb + 4 * g + i;
             if (key > row_lim[qb]) s[qb][kb][i] = -INFINITY;
+          }
+    }
+    // and keys left of the window (tiles reaching past the last row's window start)
+    if (windowed && j * BN < wrow0 + kWR + (S - T) - window) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = j * BN + 16 * kb + 4 * g + i;
+            if (key < row_lo[qb]) s[qb][kb][i] = -INFINITY;
           }
     }
 
@@ -328,13 +347,13 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     }
     stage_barrier();
     if (j + NST - 1 < ntk) load_tile(j + NST - 1, kn, vn);
-    if (wave_live && j * BN < wave_kv_end) compute_tile(j, ks, vs);
+    if (wave_live && j * BN < wave_kv_end && (j + 1) * BN > wave_kv_lo) compute_tile(j, ks, vs);
   };
 
-  load_tile(0, k_st0, v_st0);
+  load_tile(j0, k_st0, v_st0);
   if (NST == 3) {
-    if (1 < ntk) load_tile(1, k_st1, v_st1);
-    for (int j = 0;;) {
+    if (j0 + 1 < ntk) load_tile(j0 + 1, k_st1, v_st1);
+    for (int j = j0;;) {
       step(j, k_st0, v_st0, k_st2, v_st2);
       if (++j >= ntk) break;
       step(j, k_st1, v_st1, k_st0, v_st0);
@@ -343,7 +362,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       if (++j >= ntk) break;
     }
   } else {
-    for (int j = 0;;) {
+    for (int j = j0;;) {
       step(j, k_st0, v_st0, k_st1, v_st1);
       if (++j >= ntk) break;
       step(j, k_st1, v_st1, k_st0, v_st0);
@@ -376,7 +395,8 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 template <int D, bool CAUSAL, int QB>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
+                      int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
+                      hipStream_t stream) {
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
   constexpr int kBM = 16 * QB * PrefillCfg<D>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
@@ -384,7 +404,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)grid), dim3(kThreads), 0,
                      stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S,
-                     scale_log2);
+                     scale_log2, window);
   return hipGetLastError();
 }
 
@@ -396,24 +416,25 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
 // the total work (B=8 at the same shape: 30 us instead of 28.5 us).
 template <int D, bool CAUSAL>
 hipError_t launch_rows(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
+                       int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
+                       hipStream_t stream) {
   constexpr int kBM2 = 32 * PrefillCfg<D>::WAVES;
   const long long wgs2 = (long long)((T + kBM2 - 1) / kBM2) * B * Hq;
   if (wgs2 < PREFILL_SMALL_GRID)
-    return launch_one<D, CAUSAL, 1>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
-  return launch_one<D, CAUSAL, 2>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+    return launch_one<D, CAUSAL, 1>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream);
+  return launch_one<D, CAUSAL, 2>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream);
 }
 
 }  // namespace
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int Hq, int Hkv, int T, int S, int d, float scale_log2,
-                               bool causal, hipStream_t stream) {
+                               bool causal, int window, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_rows<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                  : launch_rows<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
-  return causal ? launch_rows<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                : launch_rows<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+    return causal ? launch_rows<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream)
+                  : launch_rows<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, 0, stream);
+  return causal ? launch_rows<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream)
+                : launch_rows<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, 0, stream);
 }
 
 }  // namespace attn

@@ -24,7 +24,7 @@ __global__ __launch_bounds__(kRows)
 void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                         const float* __restrict__ v, float* __restrict__ o,
                         float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
-                        float scale_log2) {
+                        float scale_log2, int window) {
   constexpr int BN = F32Tile<D>::BN;
   constexpr int V4 = BN * D / 4;             // float4 per tile
   __shared__ __attribute__((aligned(16))) float ks[BN * D];
@@ -57,8 +57,11 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
     for (int c = 0; c < D; ++c) qv[c] = 0.f;
   }
   const int row_lim = CAUSAL ? min(row + (S - T), S - 1) : S - 1;
-  int kv_end = S;
+  // causal sliding window: keys <= row + (S - T) - window are hidden too
+  const int row_lo = (CAUSAL && window > 0) ? row + (S - T) - window + 1 : 0;
+  int kv_end = S, j0 = 0;
   if (CAUSAL) kv_end = min(S, min(q0 + kRows, T) + (S - T));
+  if (CAUSAL && window > 0) j0 = max(0, q0 + (S - T) - window + 1) / BN;
   const int ntk = (kv_end + BN - 1) / BN;
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -66,7 +69,7 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 #pragma unroll
   for (int c = 0; c < D; ++c) acc[c] = 0.f;
 
-  for (int j = 0; j < ntk; ++j) {
+  for (int j = j0; j < ntk; ++j) {
     __syncthreads();
     for (int i = threadIdx.x; i < V4; i += kRows) {
       const int key = j * BN + (i * 4) / D;
@@ -88,7 +91,7 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
       float dot = 0.f;
 #pragma unroll
       for (int c = 0; c < D; ++c) dot = __builtin_fmaf(qv[c], ks[jj * D + c], dot);
-      sc[jj] = (j * BN + jj <= row_lim) ? dot : -INFINITY;
+      sc[jj] = (j * BN + jj <= row_lim && j * BN + jj >= row_lo) ? dot : -INFINITY;
       mx = fmax2(mx, sc[jj]);
     }
     const float m_new = fmax2(m_run, mx * scale_log2);
@@ -126,13 +129,14 @@ void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k
 
 template <int D, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int Hq, int Hkv, int T, int S, float scale_log2, hipStream_t stream) {
+                      int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
+                      hipStream_t stream) {
   const long long ntq = (T + kRows - 1) / kRows;
   const long long grid = ntq * B * Hq;
   hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kRows), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(o), lse, B, Hq, Hkv, T, S,
-                     scale_log2);
+                     scale_log2, window);
   return hipGetLastError();
 }
 
@@ -140,12 +144,12 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
 
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int Hq, int Hkv, int T, int S, int d, float scale_log2,
-                              bool causal, hipStream_t stream) {
+                              bool causal, int window, hipStream_t stream) {
   if (d == 128)
-    return causal ? launch_one<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                  : launch_one<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
-  return causal ? launch_one<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream)
-                : launch_one<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, stream);
+    return causal ? launch_one<128, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream)
+                  : launch_one<128, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, 0, stream);
+  return causal ? launch_one<64, true>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream)
+                : launch_one<64, false>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, 0, stream);
 }
 
 }  // namespace attn
