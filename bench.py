@@ -22,6 +22,10 @@ Reported (one JSON line on stdout):
                  workloads (GQA B=4 T=4096 d=128; long B=1 H=32 T=16384 d=128);
   window         attn_fwd_window on the GQA causal workload with a 1024-key
                  sliding window (FLOPs over the visible pairs only);
+  chunked        attn_prefill_paged on 16 sequences of 1024..8192 cached
+                 tokens whose last 512 are the new chunk, Hq=12, Hkv=2,
+                 d=128, keys through the block table (FLOPs over the
+                 visible pairs);
   backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
                  kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
                  T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
@@ -170,6 +174,27 @@ def bench_window(tea, workloads, dev, stream, flush, window=1024):
     return {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal, "
                       f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms, "value": tf,
             "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
+            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
+
+
+def bench_chunked(tea, workloads, dev, stream, flush):
+    """attn_prefill_paged on chunked_prefill_6."""
+    import torch
+    x = workloads.chunked_prefill_6()
+    xq, kp, vp = (t.to(dev) for t in (x.q, x.k_pool, x.v_pool))
+    bt, sl, ql = (torch.from_numpy(a).to(dev) for a in (x.block_table, x.seq_lens, x.q_lens))
+    xo = torch.empty_like(xq)
+    xl = torch.empty((x.N, x.Hq, x.T), dtype=torch.float32, device=dev)
+    ms, n = timed_launches(stream, flush, lambda: tea.attn_prefill_paged(
+        xq, kp, vp, bt, sl, ql, xo, xl, x.scale, stream=stream))
+    pairs = sum(int(L) * int(T) - int(T) * (int(T) - 1) // 2
+                for L, T in zip(x.seq_lens, x.q_lens))   # row i sees L - T + i + 1 keys
+    fl = 4 * x.d * x.Hq * pairs
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, chunk {x.T}, cached "
+                      f"{int(x.seq_lens.min())}..{int(x.seq_lens.max())} tokens, d={x.d}, bf16, "
+                      f"16-token pages", "kernel": "prefill_bf16_kernel (paged)", "ms": ms,
+            "value": tf, "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
             "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
 
 
@@ -451,6 +476,7 @@ def main():
         out["prefill_other"] = other
     if not args.no_next:
         out["window"] = bench_window(tea, workloads, dev, stream, flush)
+        out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush)
     if not args.no_backward:
         out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
                                          None if args.no_cpu_baseline else args.cpu_budget / 3)

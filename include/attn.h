@@ -11,6 +11,8 @@
  *   attn_bwd           the gradients dQ, dK, dV of attn_fwd's output for a
  *                      given output gradient dO, rebuilding the probabilities
  *                      tile by tile from the saved log-sum-exp.
+ *   attn_prefill_paged chunked prefill: the new query tokens of each sequence
+ *                      against its paged key/value cache, causal.
  *   attn_decode_paged  decode: one query token per sequence against a key/value
  *                      cache stored in fixed-size pages reached through a
  *                      block table.
@@ -160,6 +162,50 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
  * B=4, Hq=12, Hkv=2, T=S=4096, d=128 (n = 2); 0.4 MB with n = 1 at B=8,
  * Hq=Hkv=12, T=S=1024, d=64. */
 size_t attn_bwd_workspace_size(int B, int Hq, int Hkv, int T, int S, int d);
+
+/*
+ * attn_prefill_paged -- chunked prefill: new query tokens of each sequence
+ * against its paged KV cache, causal.
+ *
+ *   q           [N, Hq, T, d]                    bf16   queries; sequence n uses
+ *                                                       rows 0 .. q_lens[n]-1
+ *   k_pool      [num_pages, Hkv, page, d]        bf16   key pages
+ *   v_pool      [num_pages, Hkv, page, d]        bf16   value pages
+ *   block_table [N, max_blocks]                  int32  physical page of each
+ *                                                       logical block
+ *   seq_lens    [N]                              int32  cached tokens per sequence,
+ *                                                       the new ones included
+ *   q_lens      [N]                              int32  new tokens per sequence
+ *   o           [N, Hq, T, d]                    bf16   output rows 0 .. q_lens[n]-1
+ *                                                       (written; other rows untouched)
+ *   lse         [N, Hq, T]                       float32 log-sum-exp of the same
+ *                                                       rows (written); may be NULL
+ *
+ * The new tokens are the last q_lens[n] of the seq_lens[n] cached ones: row
+ * i of sequence n is the query at position p = seq_lens[n] - q_lens[n] + i
+ * and attends the cached keys j <= p (j > p - window too if window > 0), the
+ * bottom-right causal rule of attn_fwd with T = q_lens[n], S = seq_lens[n].
+ * Keys and values are read through the block table as in attn_decode_paged
+ * ("Fast attention kernels and operator fusion accelerate AI models",
+ * section on paged attention: a block table maps logical blocks to physical
+ * ones); the pages must therefore already hold the new tokens' keys and
+ * values.  Key tiles are loaded page by page straight into on-chip memory.
+ *
+ * Requirements checked on the host: N, Hq, Hkv, T, num_pages, max_blocks
+ * >= 1; Hq % Hkv == 0; window >= 0; scale finite and > 0; pointers aligned
+ * as for attn_decode_paged; o and lse overlap no input or each other.
+ * page must be 16, d 64 or 128 and dtype ATTN_BF16, else ATTN_EUNSUPPORTED.
+ * Device contents are a caller contract: 1 <= q_lens[n] <= min(T, seq_lens[n]),
+ * seq_lens[n] <= max_blocks * page, block_table[n, b] in [0, num_pages) for
+ * b < ceil(seq_lens[n] / page).  The kernels never read outside the pool
+ * (an out-of-range page id is clamped; that sequence's output is then
+ * unspecified) and write nothing for a sequence with q_lens[n] <= 0.
+ */
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens,
+                       const int32_t* q_lens, void* o, float* lse,
+                       int N, int Hq, int Hkv, int T, int d, int page, int num_pages,
+                       int max_blocks, float scale, int window, int dtype, void* stream);
 
 /*
  * attn_decode_paged -- one query token per sequence against a paged KV cache.

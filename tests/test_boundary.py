@@ -27,7 +27,8 @@ def _declared_functions():
 def test_header_declares_the_expected_entry_points():
     assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
                                      "attn_decode_workspace_size", "attn_fwd", "attn_fwd_window",
-                                     "attn_last_error", "attn_status_string"]
+                                     "attn_last_error", "attn_prefill_paged",
+                                     "attn_status_string"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -130,6 +131,40 @@ def _fwd_window(window, **kw):
 def test_fwd_window_rejects_bad_arguments(window, bad, code):
     assert _fwd_window(window, **bad) == code
     assert tea.attn_last_error().startswith("attn_fwd_window")
+
+
+# --- attn_prefill_paged argument checks ------------------------------------------
+
+PP_OK = dict(q=P, k=2 * P, v=3 * P, bt=4 * P, lens=5 * P, qlens=6 * P, o=7 * P, lse=8 * P, N=4,
+             Hq=12, Hkv=2, T=64, d=128, page=16, num_pages=100, max_blocks=32, scale=0.088,
+             window=0, dtype=ATTN_BF16, stream=None)
+
+
+def _pp(**kw):
+    a = dict(PP_OK)
+    a.update(kw)
+    return tea.lib().attn_prefill_paged(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["qlens"],
+                                        a["o"], a["lse"], a["N"], a["Hq"], a["Hkv"], a["T"],
+                                        a["d"], a["page"], a["num_pages"], a["max_blocks"],
+                                        a["scale"], a["window"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), ATTN_EINVAL), (dict(bt=None), ATTN_EINVAL), (dict(qlens=None), ATTN_EINVAL),
+    (dict(o=None), ATTN_EINVAL),
+    (dict(N=0), ATTN_EINVAL), (dict(T=0), ATTN_EINVAL), (dict(num_pages=0), ATTN_EINVAL),
+    (dict(max_blocks=0), ATTN_EINVAL), (dict(Hq=12, Hkv=5), ATTN_EINVAL),
+    (dict(window=-1), ATTN_EINVAL), (dict(scale=0.0), ATTN_EINVAL),
+    (dict(dtype=ATTN_F32), ATTN_EUNSUPPORTED), (dict(page=32), ATTN_EUNSUPPORTED),
+    (dict(d=96), ATTN_EUNSUPPORTED),
+    (dict(q=P + 4), ATTN_EINVAL), (dict(qlens=6 * P + 2), ATTN_EINVAL),
+    (dict(o=P), ATTN_EINVAL),                   # output aliases q
+    (dict(lse=7 * P + 256), ATTN_EINVAL),       # lse inside o
+    (dict(o=5 * P), ATTN_EINVAL),               # output over seq_lens
+])
+def test_prefill_paged_rejects_bad_arguments(bad, code):
+    assert _pp(**bad) == code
+    assert tea.attn_last_error().startswith("attn_prefill_paged")
 
 
 # --- attn_bwd argument checks ---------------------------------------------------

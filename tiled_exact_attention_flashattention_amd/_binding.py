@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_window.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, i32,
                                   vp]
     L.attn_fwd_window.restype = i32
+    L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                     i32, i32, f32, i32, i32, vp]
+    L.attn_prefill_paged.restype = i32
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                            i32, i32, vp, sz, vp]
     L.attn_bwd.restype = i32
@@ -240,6 +243,37 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: f
                                  N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
                                  float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes,
                                  _stream_ptr(q.device, stream))
+    _check(st)
+
+
+def attn_prefill_paged(q, k_pool, v_pool, block_table, seq_lens, q_lens, o, lse, scale: float,
+                       window: int = 0, page: int = PAGE, stream=None) -> None:
+    """Enqueue attn_prefill_paged on ``stream``.
+
+    q/o [N,Hq,T,d] bf16; pools [num_pages,Hkv,page,d] bf16; block_table int32
+    [N,max_blocks]; seq_lens, q_lens int32 [N]; lse float32 [N,Hq,T] or None.
+    """
+    import torch
+    _require_device_tensors(q, k_pool, v_pool, block_table, seq_lens, q_lens, o, lse)
+    N, Hq, T, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    if k_pool.shape != (num_pages, Hkv, page, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [num_pages, Hkv, page, d]")
+    if o.shape != q.shape or block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("shape mismatch among q, o, block_table")
+    for t in (block_table, seq_lens, q_lens):
+        if t.dtype != torch.int32:
+            raise TypeError("block_table, seq_lens and q_lens must be int32")
+    if seq_lens.shape != (N,) or q_lens.shape != (N,):
+        raise ValueError("seq_lens and q_lens must be [N]")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq, T)):
+        raise ValueError("lse must be float32 [N, Hq, T]")
+    st = lib().attn_prefill_paged(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                  block_table.data_ptr(), seq_lens.data_ptr(), q_lens.data_ptr(),
+                                  o.data_ptr(), lse.data_ptr() if lse is not None else None,
+                                  N, Hq, Hkv, T, d, page, num_pages, block_table.shape[1],
+                                  float(scale), int(window), _dtype_code(q),
+                                  _stream_ptr(q.device, stream))
     _check(st)
 
 

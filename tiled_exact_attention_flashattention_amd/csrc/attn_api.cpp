@@ -213,6 +213,55 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
   return ATTN_OK;
 }
 
+int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
+                       const int32_t* block_table, const int32_t* seq_lens, const int32_t* q_lens,
+                       void* o, float* lse, int N, int Hq, int Hkv, int T, int d, int page,
+                       int num_pages, int max_blocks, float scale, int window, int dtype,
+                       void* stream) {
+  const char* fn = "attn_prefill_paged";
+  if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !o)
+    return fail(ATTN_EINVAL, "%s: tensor pointers must be non-NULL", fn);
+  if (N < 1 || Hq < 1 || Hkv < 1 || T < 1 || d < 1 || num_pages < 1 || max_blocks < 1 || page < 1)
+    return fail(ATTN_EINVAL, "%s: sizes must be >= 1", fn);
+  if (Hq % Hkv != 0) return fail(ATTN_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
+  if (window < 0) return fail(ATTN_EINVAL, "%s: window must be >= 0", fn);
+  if (!std::isfinite(scale) || !(scale > 0.f))
+    return fail(ATTN_EINVAL, "%s: scale must be finite and > 0", fn);
+  if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "%s: only bf16 is supported", fn);
+  if (page != kPage) return fail(ATTN_EUNSUPPORTED, "%s: page size %d (need 16)", fn, page);
+  if (d != 64 && d != 128) return fail(ATTN_EUNSUPPORTED, "%s: head dim %d (need 64 or 128)", fn, d);
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+      !aligned(block_table, 4) || !aligned(seq_lens, 4) || !aligned(q_lens, 4) ||
+      (lse && !aligned(lse, 4)))
+    return fail(ATTN_EINVAL, "%s: misaligned pointer", fn);
+  const int64_t qn = (int64_t)N * Hq * T * d, pn = (int64_t)num_pages * Hkv * kPage * d;
+  if (qn > kMaxElems || pn > kMaxElems || (int64_t)T * d >= kMaxHeadElems ||
+      (int64_t)max_blocks * kPage > 0x7fffffff)
+    return fail(ATTN_EINVAL, "%s: tensor too large", fn);
+  if (((int64_t)T + 127) / 128 * N * Hq > 0x7fffffff)
+    return fail(ATTN_EINVAL, "%s: too many query tiles", fn);
+  const size_t qb = (size_t)qn * 2, pb = (size_t)pn * 2, lb = lse ? (size_t)N * Hq * T * 4 : 0;
+  const size_t btb = (size_t)N * max_blocks * 4, nb = (size_t)N * 4;
+  if (overlap(o, qb, q, qb) || overlap(o, qb, k_pool, pb) || overlap(o, qb, v_pool, pb) ||
+      overlap(o, qb, block_table, btb) || overlap(o, qb, seq_lens, nb) ||
+      overlap(o, qb, q_lens, nb) || overlap(lse, lb, q, qb) || overlap(lse, lb, k_pool, pb) ||
+      overlap(lse, lb, v_pool, pb) || overlap(lse, lb, block_table, btb) ||
+      overlap(lse, lb, seq_lens, nb) || overlap(lse, lb, q_lens, nb) || overlap(lse, lb, o, qb))
+    return fail(ATTN_EINVAL, "%s: o/lse overlap an input or each other", fn);
+
+  attn::PagedKv pkv;
+  pkv.block_table = block_table;
+  pkv.seq_lens = seq_lens;
+  pkv.q_lens = q_lens;
+  pkv.max_blocks = max_blocks;
+  pkv.num_pages = num_pages;
+  hipError_t e = attn::launch_prefill_paged_bf16(q, k_pool, v_pool, o, lse, pkv, N, Hq, Hkv, T, d,
+                                                 scale * kLog2e, window,
+                                                 static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", fn, hipGetErrorString(e));
+  return ATTN_OK;
+}
+
 int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                       int N, int Hq, int Hkv, int d, int page, int num_pages, int max_blocks,

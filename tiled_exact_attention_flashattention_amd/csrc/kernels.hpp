@@ -15,6 +15,23 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int B, int Hq, int Hkv, int T, int S, int d,
                                float scale_log2, bool causal, int window, hipStream_t stream);
 
+// Chunked prefill on a paged cache (causal, bf16): sequence n's T_n =
+// q_lens[n] queries (rows of q [N][Hq][T][d]) are the last T_n of its
+// seq_lens[n] cached tokens, whose keys and values sit in 16-token pages
+// [num_pages][Hkv][16][d] found through block_table [N][max_blocks].
+struct PagedKv {
+  const int32_t* block_table = nullptr;
+  const int32_t* seq_lens = nullptr;
+  const int32_t* q_lens = nullptr;
+  int max_blocks = 0;
+  int num_pages = 0;
+};
+
+hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pool, const void* v_pool,
+                                     void* o, float* lse, const PagedKv& pkv, int N, int Hq,
+                                     int Hkv, int T, int d, float scale_log2, int window,
+                                     hipStream_t stream);
+
 // Prefill, fp32 in/out, fp32 arithmetic on the vector ALUs.
 hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                               int B, int Hq, int Hkv, int T, int S, int d,

@@ -36,6 +36,16 @@ __device__ __forceinline__ void lds_dma4(const void* sbase, uint32_t voff, uint3
                :: "v"(voff), "s"(sbase), "s"(lds_base) : "memory");
 }
 
+// A pointer every lane holds the same value of, moved to scalar registers
+// (the base operand of the loads above must be scalar; inside a divergent
+// branch the compiler may otherwise keep it in vector registers).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }

@@ -77,12 +77,12 @@ __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) 
 // 2^kLazyTau, far inside bf16 and fp32 range.
 constexpr float kLazyTau = 8.f;
 
-template <int D, bool CAUSAL, int QB>
+template <int D, bool CAUSAL, int QB, bool PAGED>
 __global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
-                         float scale_log2, int window) {
+                         float scale_log2, int window, const PagedKv pkv) {
   constexpr int BN = PrefillCfg<D>::BN;
   constexpr int NST = PrefillCfg<D>::STAGES;
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
@@ -129,13 +129,22 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int b = grp / Hkv, hk = grp % Hkv, h = hk * hpg + hgi;
   const int qt = CAUSAL ? (ntq - 1 - rank) : rank;   // longest causal rows first
   const int q0 = qt * kBM;
+  // T is the row stride of q, o and lse.  On a paged cache sequence b has
+  // its own lengths: S cached keys, of which the last T_n are this call's
+  // queries (rows 0 .. T_n - 1 of its T); rows past T_n are not computed.
+  const int Tst = T;
+  if (PAGED) {
+    S = min(max(pkv.seq_lens[b], 0), pkv.max_blocks * 16);
+    T = min(max(pkv.q_lens[b], 0), min(Tst, S));
+    if (q0 >= T) return;                             // whole workgroup: no barrier passed yet
+  }
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
 
-  const size_t qbase = ((size_t)(b * Hq + h) * T) * D;
-  const size_t kvbase = ((size_t)(b * Hkv + hk) * S) * D;
+  const size_t qbase = ((size_t)(b * Hq + h) * Tst) * D;
+  const size_t kvbase = PAGED ? 0 : ((size_t)(b * Hkv + hk) * S) * D;
 
   // ---- keys this workgroup / wave can see ----
   const int wrow0 = q0 + kWR * wave;                 // first row of this wave
@@ -174,10 +183,46 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     koff[r] = (uint32_t)(row * D + (cph ^ k_swz<D>(row)) * 8) * 2u;
     voff[r] = (uint32_t)(row * D + (cph ^ v_swz<D>(row)) * 8) * 2u;
   }
+  // Paged cache: the rows of one load instruction (64 lanes x 16 bytes = 4
+  // rows at D=128, 8 at D=64, aligned) lie in one 16-token page, so the page
+  // is wave-uniform per instruction and its base a scalar address; the lane
+  // adds its slot.  Each wave streams the BN/16 page ids of tile j into its
+  // own LDS slot (j & 1) with a direct-to-LDS load two steps before tile j's
+  // keys are loaded, so the per-step vector-memory wait covers them (a plain
+  // load would be waited on, together with the tile loads in flight, where
+  // it is used).  Rows past S re-read row S-1, in the same page as the
+  // instruction's clamped first row.
+  static_assert(!PAGED || NST == 2, "the page-id stream assumes a two-stage ring");
+  constexpr int kRowsPerLoad = 64 / CPR;
+  constexpr int kIds = BN / 16;
+  __shared__ int32_t pg_ids[PAGED ? 2 * PrefillCfg<D>::WAVES * 8 : 1];   // [slot][wave][id]
+  const void* bt_row = PAGED ? uniform_ptr(pkv.block_table + (size_t)b * pkv.max_blocks) : nullptr;
+  auto fetch_pages = [&](int j) {
+    if (PAGED && lane < kIds) {
+      const int blk = min(j * kIds + lane, ((S + 15) >> 4) - 1);
+      lds_dma4(uniform_ptr(bt_row), (uint32_t)blk * 4u,
+               lds_addr(pg_ids) + (uint32_t)(((j & 1) * PrefillCfg<D>::WAVES + wave_s) * 32));
+    }
+  };
   auto load_tile = [&](int j, bf16* ks, bf16* vs) {
     const uint32_t kl = lds_addr(ks) + (uint32_t)(wave_s * CPW) * 1024u;
     const uint32_t vl = lds_addr(vs) + (uint32_t)(wave_s * CPW) * 1024u;
     const bool full = (j + 1) * BN <= S;
+    if (PAGED) {
+      const int32_t* ids = pg_ids + ((j & 1) * PrefillCfg<D>::WAVES + wave) * 8;
+#pragma unroll
+      for (int r = 0; r < CPW; ++r) {
+        const int key0 = min(j * BN + (wave_s * CPW + r) * kRowsPerLoad, S - 1);
+        int pg = __builtin_amdgcn_readfirstlane(ids[(key0 >> 4) - j * kIds]);
+        pg = min(max(pg, 0), pkv.num_pages - 1);     // never outside the pool
+        const size_t pbase = ((size_t)pg * Hkv + hk) * 16 * D;
+        const int key = full ? j * BN + lrow[r] : min(j * BN + lrow[r], S - 1);
+        const uint32_t slot = (uint32_t)((key & 15) - (lrow[r] & 15)) * D * 2u;
+        lds_dma16(k + pbase, koff[r] - (uint32_t)((lrow[r] & ~15) * D * 2) + slot, kl + 1024u * r);
+        lds_dma16(v + pbase, voff[r] - (uint32_t)((lrow[r] & ~15) * D * 2) + slot, vl + 1024u * r);
+      }
+      return;
+    }
 #pragma unroll
     for (int r = 0; r < CPW; ++r) {
       uint32_t add;
@@ -346,13 +391,22 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));
     }
     stage_barrier();
-    if (j + NST - 1 < ntk) load_tile(j + NST - 1, kn, vn);
+    if (j + NST - 1 < ntk) {
+      load_tile(j + NST - 1, kn, vn);
+      if (j + NST < ntk) fetch_pages(j + NST);
+    }
     if (wave_live && j * BN < wave_kv_end && (j + 1) * BN > wave_kv_lo) compute_tile(j, ks, vs);
   };
 
+  fetch_pages(j0);
+  if (PAGED) __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));   // tile j0's page ids
   load_tile(j0, k_st0, v_st0);
+  if (j0 + 1 < ntk) fetch_pages(j0 + 1);
   if (NST == 3) {
-    if (j0 + 1 < ntk) load_tile(j0 + 1, k_st1, v_st1);
+    if (j0 + 1 < ntk) {
+      load_tile(j0 + 1, k_st1, v_st1);
+      if (j0 + 2 < ntk) fetch_pages(j0 + 2);
+    }
     for (int j = j0;;) {
       step(j, k_st0, v_st0, k_st2, v_st2);
       if (++j >= ntk) break;
@@ -388,23 +442,23 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         *reinterpret_cast<bf16x4*>(op + 16 * db) = r;
       }
       if (lse != nullptr && g == 0)
-        lse[(size_t)(b * Hq + h) * T + row] = (m_run[qb] + log2f(l_tot)) * kLn2;
+        lse[(size_t)(b * Hq + h) * Tst + row] = (m_run[qb] + log2f(l_tot)) * kLn2;
     }
   }
 }
 
-template <int D, bool CAUSAL, int QB>
+template <int D, bool CAUSAL, int QB, bool PAGED>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
-                      hipStream_t stream) {
+                      const PagedKv& pkv, hipStream_t stream) {
   constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
   constexpr int kBM = 16 * QB * PrefillCfg<D>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     stream, static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S,
-                     scale_log2, window);
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB, PAGED>), dim3((unsigned)grid),
+                     dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
+                     static_cast<const bf16*>(k), static_cast<const bf16*>(v),
+                     static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S, scale_log2, window, pkv);
   return hipGetLastError();
 }
 
@@ -414,18 +468,31 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
 // most one workgroup per CU is bound by that path (B=1 at T=1024, d=64: 11 us
 // instead of 16 us), so it gets one block per wave; a fuller grid is bound by
 // the total work (B=8 at the same shape: 30 us instead of 28.5 us).
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool PAGED = false>
 hipError_t launch_rows(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
-                       hipStream_t stream) {
+                       hipStream_t stream, const PagedKv& pkv = PagedKv{}) {
   constexpr int kBM2 = 32 * PrefillCfg<D>::WAVES;
   const long long wgs2 = (long long)((T + kBM2 - 1) / kBM2) * B * Hq;
   if (wgs2 < PREFILL_SMALL_GRID)
-    return launch_one<D, CAUSAL, 1>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream);
-  return launch_one<D, CAUSAL, 2>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window, stream);
+    return launch_one<D, CAUSAL, 1, PAGED>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window,
+                                           pkv, stream);
+  return launch_one<D, CAUSAL, 2, PAGED>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window,
+                                         pkv, stream);
 }
 
 }  // namespace
+
+hipError_t launch_prefill_paged_bf16(const void* q, const void* k_pool, const void* v_pool,
+                                     void* o, float* lse, const PagedKv& pkv, int N, int Hq,
+                                     int Hkv, int T, int d, float scale_log2, int window,
+                                     hipStream_t stream) {
+  if (d == 128)
+    return launch_rows<128, true, true>(q, k_pool, v_pool, o, lse, N, Hq, Hkv, T, 0, scale_log2,
+                                        window, stream, pkv);
+  return launch_rows<64, true, true>(q, k_pool, v_pool, o, lse, N, Hq, Hkv, T, 0, scale_log2,
+                                     window, stream, pkv);
+}
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                                int B, int Hq, int Hkv, int T, int S, int d, float scale_log2,

@@ -31,6 +31,10 @@ Backward inputs (``make_backward``) draw q, k, v exactly as ``make_prefill``
 and then the output gradient dO, float32 ``standard_normal`` of q's shape,
 rounded to bf16.  ``backward_3`` is the gradient pass of prefill_3: its q, k,
 v are prefill_3's (same seed), with dO drawn after them.
+
+``make_prefill_paged`` lays chunked-prefill inputs out like ``make_decode``;
+``chunked_prefill_6`` is its benchmark case: 16 sequences with 1024..8192
+cached tokens whose last 512 are the chunk, on the decode model shape.
 """
 from __future__ import annotations
 
@@ -69,6 +73,30 @@ class BackwardInputs(PrefillInputs):
 
     def f64(self):
         return super().f64() + (self.do.double().numpy(),)
+
+
+@dataclass
+class PagedPrefillInputs:
+    N: int
+    Hq: int
+    Hkv: int
+    T: int                      # row stride of q / o (largest chunk)
+    d: int
+    page: int
+    num_pages: int
+    max_blocks: int
+    scale: float
+    window: int
+    seq_lens: np.ndarray        # int32 [N], cached tokens incl. the chunk
+    q_lens: np.ndarray          # int32 [N], chunk tokens (the last of seq_lens)
+    block_table: np.ndarray     # int32 [N, max_blocks], -1 past the end
+    q: object                   # torch CPU bf16 [N, Hq, T, d]
+    k_pool: object              # torch CPU bf16 [num_pages, Hkv, page, d]
+    v_pool: object
+    name: str = ""
+
+    def f64(self):
+        return (self.q.double().numpy(), self.k_pool.double().numpy(), self.v_pool.double().numpy())
 
 
 @dataclass
@@ -185,6 +213,56 @@ def make_decode(N, Hq, Hkv, d, min_len, max_len, page=PAGE, max_blocks=None, see
                         name=name, meta={"numpy": np.__version__, "sum_len": int(seq_lens.sum())})
 
 
+def make_prefill_paged(N, Hq, Hkv, T, d, min_len, max_len, q_lens=None, lens=None, page=PAGE,
+                       window=0, seed=0, poison_tail=False, extra_pages=0, name=""):
+    """Chunked-prefill inputs on a paged cache.
+
+    Draws, in order: cached lengths (discrete uniform [min_len, max_len],
+    overridden by ``lens``), chunk lengths (uniform [1, min(T, len)], unless
+    ``q_lens`` is given: an int for all or a list), one permutation of the
+    pool (the sequences' pages plus ``extra_pages`` unused ones), then q,
+    k_pool, v_pool iid N(0,1).  Page layout and the -1 padding of the block
+    table are those of ``make_decode``; ``poison_tail`` sets the unused slots
+    of every last page to NaN.
+    """
+    rng = np.random.default_rng(seed)
+    drawn = rng.integers(min_len, max_len + 1, N)
+    seq_lens = np.asarray(drawn if lens is None else lens, dtype=np.int64)
+    drawn_q = rng.integers(1, np.minimum(T, seq_lens) + 1)
+    if q_lens is None:
+        ql = drawn_q
+    elif np.isscalar(q_lens):
+        ql = np.full(N, int(q_lens))
+    else:
+        ql = np.asarray(q_lens)
+    ql = np.asarray(ql, dtype=np.int64)
+    assert (ql >= 1).all() and (ql <= np.minimum(T, seq_lens)).all()
+    pages_per = (seq_lens + page - 1) // page
+    max_blocks = int(pages_per.max())
+    P = int(pages_per.sum()) + extra_pages
+    perm = rng.permutation(P)
+    block_table = np.full((N, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for n in range(N):
+        cnt = int(pages_per[n])
+        block_table[n, :cnt] = perm[off:off + cnt]
+        off += cnt
+    q = rng.standard_normal((N, Hq, T, d), dtype=np.float32)
+    k_pool = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+    v_pool = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+    if poison_tail:
+        for n in range(N):
+            used = int(seq_lens[n]) - (int(pages_per[n]) - 1) * page
+            if used < page:
+                last = block_table[n, int(pages_per[n]) - 1]
+                k_pool[last, :, used:, :] = np.nan
+                v_pool[last, :, used:, :] = np.nan
+    return PagedPrefillInputs(N, Hq, Hkv, T, d, page, P, max_blocks, 1.0 / math.sqrt(d), window,
+                              seq_lens.astype(np.int32), ql.astype(np.int32), block_table,
+                              _cast(q, "bf16"), _cast(k_pool, "bf16"), _cast(v_pool, "bf16"),
+                              name=name)
+
+
 # --- the five named workloads -------------------------------------------------
 
 def prefill_1():
@@ -209,6 +287,13 @@ def decode_5(poison_tail=False):
                        poison_tail=poison_tail, name="decode_5")
 
 
+def chunked_prefill_6():
+    """Chunked prefill on the decode model shape: 16 sequences, chunks of 512
+    new tokens at the end of 1024..8192 cached ones, Hq=12, Hkv=2, d=128."""
+    return make_prefill_paged(16, 12, 2, 512, 128, 1024, 8192, q_lens=512, seed=1006,
+                              name="chunked_prefill_6")
+
+
 def backward_3():
     """The gradient pass of prefill_3 (same q, k, v), dO drawn after v."""
     return make_backward(4, 12, 2, 4096, 4096, 128, causal=True, seed=1003, name="backward_3")
@@ -221,6 +306,7 @@ WORKLOADS = {
     "prefill_4": prefill_4,
     "decode_5": decode_5,
     "backward_3": backward_3,
+    "chunked_prefill_6": chunked_prefill_6,
 }
 
 # Human-readable shapes, used for labels in the benchmark output.
@@ -231,4 +317,6 @@ SHAPES = {
     "prefill_4": dict(B=1, Hq=32, Hkv=32, T=16384, S=16384, d=128, dtype="bf16", causal=True),
     "decode_5": dict(N=64, Hq=12, Hkv=2, d=128, page=16, min_len=512, max_len=8192, dtype="bf16"),
     "backward_3": dict(B=4, Hq=12, Hkv=2, T=4096, S=4096, d=128, dtype="bf16", causal=True),
+    "chunked_prefill_6": dict(N=16, Hq=12, Hkv=2, T=512, d=128, page=16, min_len=1024,
+                              max_len=8192, dtype="bf16"),
 }
