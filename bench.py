@@ -26,6 +26,9 @@ Reported (one JSON line on stdout):
                  tokens whose last 512 are the new chunk, Hq=12, Hkv=2,
                  d=128, keys through the block table (FLOPs over the
                  visible pairs);
+  decode_fp8     attn_decode_paged_fp8 on decode_5's shape with E4M3 pages
+                 (decode_fp8_7): GB/s over the bytes it must read (one byte
+                 per cached K/V element, plus q, o, lse, lengths, block table);
   backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
                  kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
                  T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
@@ -196,6 +199,29 @@ def bench_chunked(tea, workloads, dev, stream, flush):
                       f"16-token pages", "kernel": "prefill_bf16_kernel (paged)", "ms": ms,
             "value": tf, "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
             "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
+
+
+def bench_decode_fp8(tea, workloads, dev, stream, flush):
+    """attn_decode_paged_fp8 on decode_fp8_7 (stream + combine kernels)."""
+    import torch
+    x = workloads.decode_fp8_7()
+    xq, kc, vc = x.q.to(dev), x.k_codes.to(dev), x.v_codes.to(dev)
+    bt, sl = torch.from_numpy(x.block_table).to(dev), torch.from_numpy(x.seq_lens).to(dev)
+    xo = torch.empty_like(xq)
+    xl = torch.empty((x.N, x.Hq), dtype=torch.float32, device=dev)
+    ws = tea.decode_workspace(x.N, x.Hq, x.d, x.max_blocks, dev)
+    ms, n = timed_launches(stream, flush, lambda: tea.attn_decode_paged_fp8(
+        xq, kc, vc, x.k_scale, x.v_scale, bt, sl, xo, xl, x.scale, ws, stream=stream), n=12)
+    tokens = int(x.seq_lens.astype("int64").sum())
+    pages = int(((x.seq_lens.astype("int64") + x.page - 1) // x.page).sum())
+    nbytes = tokens * x.Hkv * x.d * 2 + 2 * x.N * x.Hq * x.d * 2 + x.N * x.Hq * 4 + x.N * 4 + pages * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, E4M3 K/V pages, lengths "
+                      f"U[512,8192] (sum {tokens})", "kernel": "decode_stream_kernel<fp8>+"
+                      "decode_combine_kernel", "ms": ms, "value": gbs, "unit": "GB/s",
+            "algorithmic_bytes": nbytes, "bound": "hbm", "peak": PEAK_HBM_GBS,
+            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": n,
+            "tokens_per_s": tokens / (ms * 1e-3)}
 
 
 def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
@@ -477,6 +503,7 @@ def main():
     if not args.no_next:
         out["window"] = bench_window(tea, workloads, dev, stream, flush)
         out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush)
+        out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush)
     if not args.no_backward:
         out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
                                          None if args.no_cpu_baseline else args.cpu_budget / 3)

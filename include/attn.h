@@ -16,6 +16,7 @@
  *   attn_decode_paged  decode: one query token per sequence against a key/value
  *                      cache stored in fixed-size pages reached through a
  *                      block table.
+ *   attn_decode_paged_fp8  the same over fp8 (E4M3) pages with scales.
  *
  * Definitions (page titles and sections of the sources):
  *   - "Advanced Attention Mechanisms - II" (A. Das), section Tiling, steps 1-3:
@@ -253,6 +254,36 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int N, int Hq, int Hkv, int d, int page, int num_pages,
                       int max_blocks, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_fp8 -- attn_decode_paged over fp8 key/value pages.
+ *
+ *   k_pool, v_pool  [num_pages, Hkv, page, d]  uint8  E4M3 codes (OCP 8-bit
+ *                   floating point, "fn" variant: sign, 4 exponent bits with
+ *                   bias 7, 3 mantissa bits, no infinities, S.1111.111 NaN)
+ *   k_scale, v_scale  float  per-tensor scales: K = k_scale * e4m3(code),
+ *                            V = v_scale * e4m3(code)
+ *   every other argument as for attn_decode_paged (q and o bf16; the same
+ *   workspace size, attn_decode_workspace_size).
+ *
+ * "Fast attention kernels and operator fusion accelerate AI models",
+ * section on kernel fusion: dequantisation is fused into the matrix product
+ * that consumes it.  Here the codes are widened to bf16 (exactly: every
+ * E4M3 value is a bf16 value) in registers right before the MFMAs; k_scale
+ * folds into the logit scale and v_scale into the output normalisation, so
+ * the result is attn_decode_paged's definition on the dequantised cache,
+ * with half the bytes per token read from HBM.  A NaN code in a used slot
+ * gives NaN results; slots past a sequence's length are never used.
+ *
+ * Requirements: as for attn_decode_paged, plus k_scale and v_scale finite
+ * and > 0 (else ATTN_EINVAL), and k_pool, v_pool 16-byte aligned.
+ */
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
+                          float k_scale, float v_scale, const int32_t* block_table,
+                          const int32_t* seq_lens, void* o, float* lse,
+                          int N, int Hq, int Hkv, int d, int page, int num_pages,
+                          int max_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid):
  * r(N * Hq * 8) (which workers hold each sequence's pieces)

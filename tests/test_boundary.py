@@ -26,9 +26,9 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
-                                     "attn_decode_workspace_size", "attn_fwd", "attn_fwd_window",
-                                     "attn_last_error", "attn_prefill_paged",
-                                     "attn_status_string"]
+                                     "attn_decode_paged_fp8", "attn_decode_workspace_size",
+                                     "attn_fwd", "attn_fwd_window", "attn_last_error",
+                                     "attn_prefill_paged", "attn_status_string"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -260,6 +260,28 @@ def _dec(**kw):
 def test_decode_rejects_bad_arguments(bad, code):
     assert _dec(**bad) == code
     assert tea.attn_last_error().startswith("attn_decode_paged")
+
+
+def _dec8(k_scale=0.03, v_scale=0.03, **kw):
+    a = dict(DEC_OK)
+    a.update(kw)
+    return tea.lib().attn_decode_paged_fp8(a["q"], a["k"], a["v"], k_scale, v_scale, a["bt"],
+                                           a["lens"], a["o"], a["lse"], a["N"], a["Hq"], a["Hkv"],
+                                           a["d"], a["page"], a["num_pages"], a["max_blocks"],
+                                           a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("scales,bad,code", [
+    ((0.0, 0.03), {}, ATTN_EINVAL), ((0.03, -1.0), {}, ATTN_EINVAL),
+    ((float("nan"), 0.03), {}, ATTN_EINVAL), ((0.03, float("inf")), {}, ATTN_EINVAL),
+    ((1e38, 0.03), dict(scale=1e3), ATTN_EINVAL),          # scale * k_scale overflows
+    ((0.03, 0.03), dict(q=None), ATTN_EINVAL), ((0.03, 0.03), dict(page=8), ATTN_EUNSUPPORTED),
+    ((0.03, 0.03), dict(d=96), ATTN_EUNSUPPORTED), ((0.03, 0.03), dict(ws_bytes=WS - 1), ATTN_EINVAL),
+    ((0.03, 0.03), dict(k=2 * P + 8), ATTN_EINVAL), ((0.03, 0.03), dict(Hq=34, Hkv=2), ATTN_EUNSUPPORTED),
+])
+def test_decode_fp8_rejects_bad_arguments(scales, bad, code):
+    assert _dec8(*scales, **bad) == code
+    assert tea.attn_last_error().startswith("attn_decode_paged_fp8")
 
 
 def test_python_binding_rejects_host_tensors():

@@ -262,50 +262,83 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
   return ATTN_OK;
 }
 
-int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
-                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
-                      int N, int Hq, int Hkv, int d, int page, int num_pages, int max_blocks,
-                      float scale, int dtype, void* workspace, size_t workspace_bytes,
-                      void* stream) {
+}  // extern "C"
+
+namespace {
+
+// attn_decode_paged and attn_decode_paged_fp8 (fp8: E4M3 pools with scales).
+int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, const void* v_pool,
+                  float k_scale, float v_scale, const int32_t* block_table,
+                  const int32_t* seq_lens, void* o, float* lse, int N, int Hq, int Hkv, int d,
+                  int page, int num_pages, int max_blocks, float scale, int dtype,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
-    return fail(ATTN_EINVAL, "attn_decode_paged: tensor pointers must be non-NULL");
+    return fail(ATTN_EINVAL, "%s: tensor pointers must be non-NULL", fn);
   if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1 || max_blocks < 1 || page < 1)
-    return fail(ATTN_EINVAL, "attn_decode_paged: sizes must be >= 1");
+    return fail(ATTN_EINVAL, "%s: sizes must be >= 1", fn);
   if (Hq % Hkv != 0)
-    return fail(ATTN_EINVAL, "attn_decode_paged: Hq=%d is not a multiple of Hkv=%d", Hq, Hkv);
+    return fail(ATTN_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (!std::isfinite(scale) || !(scale > 0.f))
-    return fail(ATTN_EINVAL, "attn_decode_paged: scale must be finite and > 0");
-  if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: only bf16 is supported");
-  if (page != kPage) return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: page size %d (need 16)", page);
+    return fail(ATTN_EINVAL, "%s: scale must be finite and > 0", fn);
+  if (fp8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
+              !(v_scale > 0.f) || !std::isfinite(scale * k_scale * kLog2e)))
+    return fail(ATTN_EINVAL, "%s: k_scale and v_scale must be finite and > 0", fn);
+  if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "%s: only bf16 queries are supported", fn);
+  if (page != kPage) return fail(ATTN_EUNSUPPORTED, "%s: page size %d (need 16)", fn, page);
   if (d != 64 && d != 128)
-    return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: head dim %d (need 64 or 128)", d);
+    return fail(ATTN_EUNSUPPORTED, "%s: head dim %d (need 64 or 128)", fn, d);
   if (Hq / Hkv > 16)
-    return fail(ATTN_EUNSUPPORTED, "attn_decode_paged: %d query heads per KV head (max 16)", Hq / Hkv);
+    return fail(ATTN_EUNSUPPORTED, "%s: %d query heads per KV head (max 16)", fn, Hq / Hkv);
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
       !aligned(block_table, 4) || !aligned(seq_lens, 4) || (lse && !aligned(lse, 4)))
-    return fail(ATTN_EINVAL, "attn_decode_paged: misaligned pointer");
+    return fail(ATTN_EINVAL, "%s: misaligned pointer", fn);
   if ((int64_t)max_blocks * kPage > 0x7fffffff || (int64_t)num_pages * Hkv * kPage * d > kMaxElems)
-    return fail(ATTN_EINVAL, "attn_decode_paged: cache too large");
+    return fail(ATTN_EINVAL, "%s: cache too large", fn);
   if ((int64_t)N * Hq > 0x7fffffff / 1024 || N > 65535 || Hkv > 65535)
-    return fail(ATTN_EINVAL, "attn_decode_paged: N, Hkv or N*Hq too large");
+    return fail(ATTN_EINVAL, "%s: N, Hkv or N*Hq too large", fn);
   if ((int64_t)N * Hkv * ((max_blocks + 1) / 2) > 0x7fffffff)
-    return fail(ATTN_EINVAL, "attn_decode_paged: too many page pairs (N*Hkv*max_blocks/2 >= 2^31)");
+    return fail(ATTN_EINVAL, "%s: too many page pairs (N*Hkv*max_blocks/2 >= 2^31)", fn);
   const WsLayout lay = decode_workspace_layout(N, Hq, d);
   if (!workspace || workspace_bytes < lay.total)
-    return fail(ATTN_EINVAL, "attn_decode_paged: workspace of %zu bytes needed, %zu given",
-                lay.total, workspace_bytes);
-  if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "attn_decode_paged: misaligned workspace");
+    return fail(ATTN_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
+                workspace_bytes);
+  if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "%s: misaligned workspace", fn);
 
   char* ws = static_cast<char*>(workspace);
   attn::DecodeWorkspace dw;
   dw.seg_waves = reinterpret_cast<int2*>(ws);
   dw.o_part = reinterpret_cast<float*>(ws + lay.o_part);
   dw.lse_part = reinterpret_cast<float*>(ws + lay.lse_part);
+  const float scale_log2 = scale * kLog2e * (fp8 ? k_scale : 1.f);
   hipError_t e = attn::launch_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, dw,
-                                           N, Hq, Hkv, d, num_pages, max_blocks, scale * kLog2e,
-                                           static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(ATTN_EHIP, "attn_decode_paged: %s", hipGetErrorString(e));
+                                           N, Hq, Hkv, d, num_pages, max_blocks, scale_log2, fp8,
+                                           v_scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                      const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
+                      int N, int Hq, int Hkv, int d, int page, int num_pages, int max_blocks,
+                      float scale, int dtype, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  return decode_common("attn_decode_paged", false, q, k_pool, v_pool, 1.f, 1.f, block_table,
+                       seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks, scale, dtype,
+                       workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, float k_scale,
+                          float v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                          void* o, float* lse, int N, int Hq, int Hkv, int d, int page,
+                          int num_pages, int max_blocks, float scale, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return decode_common("attn_decode_paged_fp8", true, q, k_pool, v_pool, k_scale, v_scale,
+                       block_table, seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks,
+                       scale, ATTN_BF16, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -39,12 +39,15 @@
 // All Hq/Hkv query heads of a KV head are the 16 columns of a 16x16x32 MFMA.
 // Positions at or past the sequence length, and pages outside
 // [0, num_pages), are masked and never dereferenced.
+#include <type_traits>
+
 #include "cdna4.hpp"
 #include "kernels.hpp"
 
 namespace attn {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = 16;
 constexpr int kMinPairsPerWave = 4;   // fewer units than 4 per wave: use fewer waves
 
@@ -81,13 +84,30 @@ __device__ __forceinline__ int clamp_len(int len, int max_blocks) {
 // Stream kernel.
 
 // Registers of one page pair in flight: K as A operands, V as row chunks.
-template <int D>
-struct PairRegs {
+// With fp8 pages each 16-byte load holds 16 codes: K two k-chunks of one key
+// row, V half (D=64: all) of a row's 16-element chunk pair.
+template <int D, bool FP8> struct PairRegs;
+template <int D> struct PairRegs<D, false> {
   static constexpr int NDC = D / 32;                    // k-chunks of the S^T MFMA
   static constexpr int VCH = 2 * kPage * (D / 8) / 64;  // V chunks per lane
   bf16x8 k[2][NDC];
   u32x4 v[VCH];
 };
+template <int D> struct PairRegs<D, true> {
+  static constexpr int NDC = D / 32;
+  static constexpr int KLD = NDC / 2;                   // 16-byte K loads per page
+  static constexpr int VCH = 2 * kPage * (D / 16) / 64; // 16-byte V loads per lane
+  u32x4 k[2][KLD];
+  u32x4 v[VCH];
+};
+
+// Eight E4M3 codes (OCP "fn" format, as the conversion unit of this chip
+// reads them) to bf16; every E4M3 value is exact in bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
+  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false), b = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
+  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false), d = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+  return pack_bf16x8(a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]);
+}
 
 // One page pair, all fields wave-uniform.  n < 0 marks a padding pair.
 struct PairMeta {
@@ -95,16 +115,21 @@ struct PairMeta {
   int tv0, tv1;               // tokens of page 0 / page 1 that take part (0: masked)
 };
 
-template <int D>
+// FP8: K and V pages hold E4M3 codes; scale_log2 then includes the key
+// scale and v_scale multiplies the output (1 for bf16 pages).
+template <int D, bool FP8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
-void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ kpool,
-                          const bf16* __restrict__ vpool, const int32_t* __restrict__ block_table,
+void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ kpool_v,
+                          const void* __restrict__ vpool_v, const int32_t* __restrict__ block_table,
                           const int32_t* __restrict__ seq_lens, bf16* __restrict__ o,
                           float* __restrict__ lse, int2* __restrict__ seg_waves,
                           float* __restrict__ o_part, float* __restrict__ lse_part, int N, int Hq,
-                          int Hkv, int num_pages, int max_blocks, float scale_log2) {
-  constexpr int NDC = PairRegs<D>::NDC;
-  constexpr int VCH = PairRegs<D>::VCH;
+                          int Hkv, int num_pages, int max_blocks, float scale_log2, float v_scale) {
+  using KV = typename std::conditional<FP8, uint8_t, bf16>::type;
+  const KV* __restrict__ kpool = static_cast<const KV*>(kpool_v);
+  const KV* __restrict__ vpool = static_cast<const KV*>(vpool_v);
+  constexpr int NDC = PairRegs<D, FP8>::NDC;
+  constexpr int VCH = PairRegs<D, FP8>::VCH;
   constexpr int NDB = D / 16;                 // 16-row blocks of O^T
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
 
@@ -189,12 +214,18 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   };
 
   // ---- Q operand (B of S^T = K Q^T): column l16 = query head hk*G + l16 ----
+  // k-slots of chunk c: d = 32 c + 8 g + (0..7); with fp8 pages the order
+  // follows the 16-code K loads instead: chunk 2h + t takes d = 64 h + 16 g +
+  // 8 t + (0..7) (any order of d serves, as long as K and Q share it)
   bf16x8 qop[NDC];
   int q_n = -1, q_hk = -1;
   auto load_q = [&](int n, int hk) {
-    const bf16* qp = q + ((size_t)n * Hq + hk * G + min(l16, G - 1)) * D + 8 * g;
+    const bf16* qh = q + ((size_t)n * Hq + hk * G + min(l16, G - 1)) * D;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) qop[c] = *reinterpret_cast<const bf16x8*>(qp + 32 * c);
+    for (int c = 0; c < NDC; ++c) {
+      const int d0 = FP8 ? 64 * (c >> 1) + 16 * g + 8 * (c & 1) : 32 * c + 8 * g;
+      qop[c] = *reinterpret_cast<const bf16x8*>(qh + d0);
+    }
     if (l16 >= G) {
 #pragma unroll
       for (int c = 0; c < NDC; ++c) qop[c] = bf16x8{};
@@ -218,7 +249,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   // of loads in flight is the same on every path and the compiler's wait
   // counts stay exact.  A masked page (and a padding pair) reads page 0 of
   // KV head 0, which is in bounds and stays in L2.
-  auto issue = [&](PairRegs<D>& r, int pid, PairMeta& m) {
+  auto issue = [&](PairRegs<D, FP8>& r, int pid, PairMeta& m) {
     const int id0 = __builtin_amdgcn_readlane(pid, 0), id1 = __builtin_amdgcn_readlane(pid, 1);
     const bool ok0 = m.n >= 0 && id0 >= 0 && id0 < num_pages;
     const bool ok1 = m.n >= 0 && id1 >= 0 && id1 < num_pages;
@@ -228,24 +259,39 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     const size_t head_off = (size_t)(m.n >= 0 ? m.hk : 0) * kPage * D;
     const size_t off0 = (ok0 ? (size_t)id0 * page_stride : 0) + head_off;
     const size_t off1 = (ok1 ? (size_t)id1 * page_stride : 0) + head_off;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const bf16* kp = kpool + (p ? off1 : off0) + l16 * D + 8 * g;
+      for (int p = 0; p < 2; ++p) {
+        const KV* kp = kpool + (p ? off1 : off0) + l16 * D + 16 * g;
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) r.k[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
-    }
+        for (int h = 0; h < PairRegs<D, FP8>::KLD; ++h) r.k[p][h] = load16(kp + 64 * h);
+      }
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const bf16* vp = vpool + (p ? off1 : off0) + lane * 8;
+      for (int p = 0; p < 2; ++p) {
+        const KV* vp = vpool + (p ? off1 : off0) + lane * 16;
 #pragma unroll
-      for (int c = 0; c < VCH / 2; ++c) r.v[p * (VCH / 2) + c] = load16(vp + 64 * 8 * c);
+        for (int c = 0; c < VCH / 2; ++c) r.v[p * (VCH / 2) + c] = load16(vp + 64 * 16 * c);
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const KV* kp = kpool + (p ? off1 : off0) + l16 * D + 8 * g;
+#pragma unroll
+        for (int c = 0; c < NDC; ++c) r.k[p][c] = *reinterpret_cast<const bf16x8*>(kp + 32 * c);
+      }
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const KV* vp = vpool + (p ? off1 : off0) + lane * 8;
+#pragma unroll
+        for (int c = 0; c < VCH / 2; ++c) r.v[p * (VCH / 2) + c] = load16(vp + 64 * 8 * c);
+      }
     }
   };
 
   // Writes the result of the piece that ends with pair m and resets the state.
   auto finish_piece = [&](const PairMeta& m) {
     const float l_tot = pair_sum32(pair_sum16(l_part));
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? v_scale / l_tot : 0.f;
     const float lse_v = l_tot > 0.f ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
     const int s = m.u - m.p, e = s + m.np;
     if (s >= a && lane == 0)                  // this wave holds the segment's first pair
@@ -282,20 +328,41 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   // One pair: V to LDS, S^T = K Q^T, the online-softmax update, then
   // O^T += V^T P^T.  As soon as S has consumed K, r takes the loads of pair
   // `mp` (page ids in pid), and pid takes the ids of the pair after that.
-  auto step = [&](PairRegs<D>& r, PairMeta& mk, int& pid, PairMeta& mp) {
+  auto step = [&](PairRegs<D, FP8>& r, PairMeta& mk, int& pid, PairMeta& mp) {
     const PairMeta m = mk;
-    // V chunk c of page p is row (lane + 64 c) / CPR of that page
+    const u32x4 zero = {0, 0, 0, 0};
+    if constexpr (FP8) {
+      // V load c of page p holds codes 16 col .. +15 of row (lane + 64 c) / (D/16):
+      // bf16 chunks 2 col and 2 col + 1 of that row
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int tv = p ? m.tv1 : m.tv0;
+      for (int p = 0; p < 2; ++p) {
+        const int tv = p ? m.tv1 : m.tv0;
 #pragma unroll
-      for (int c = 0; c < VCH / 2; ++c) {
-        const int ch = lane + 64 * c;
-        const int slot = ch / CPR, col = ch % CPR;
-        const int row = 16 * p + slot;
-        const u32x4 zero = {0, 0, 0, 0};
-        *reinterpret_cast<u32x4*>(vl + row * D + (col ^ dv_swz<D>(row)) * 8) =
-            slot < tv ? r.v[p * (VCH / 2) + c] : zero;
+        for (int c = 0; c < VCH / 2; ++c) {
+          const int ch = lane + 64 * c;
+          const int slot = ch / (D / 16), col = ch % (D / 16);
+          const int row = 16 * p + slot;
+          const u32x4 raw = r.v[p * (VCH / 2) + c];
+          const bf16x8 lo = e4m3x8_to_bf16(raw[0], raw[1]), hi = e4m3x8_to_bf16(raw[2], raw[3]);
+          *reinterpret_cast<u32x4*>(vl + row * D + ((2 * col) ^ dv_swz<D>(row)) * 8) =
+              slot < tv ? *reinterpret_cast<const u32x4*>(&lo) : zero;
+          *reinterpret_cast<u32x4*>(vl + row * D + ((2 * col + 1) ^ dv_swz<D>(row)) * 8) =
+              slot < tv ? *reinterpret_cast<const u32x4*>(&hi) : zero;
+        }
+      }
+    } else {
+      // V chunk c of page p is row (lane + 64 c) / CPR of that page
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const int tv = p ? m.tv1 : m.tv0;
+#pragma unroll
+        for (int c = 0; c < VCH / 2; ++c) {
+          const int ch = lane + 64 * c;
+          const int slot = ch / CPR, col = ch % CPR;
+          const int row = 16 * p + slot;
+          *reinterpret_cast<u32x4*>(vl + row * D + (col ^ dv_swz<D>(row)) * 8) =
+              slot < tv ? r.v[p * (VCH / 2) + c] : zero;
+        }
       }
     }
     // A new segment needs its query rows.  The wait for them is taken inside
@@ -312,7 +379,16 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
     for (int p = 0; p < 2; ++p) {
       s[p] = f32x4{};
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) s[p] = mfma_16x16x32(r.k[p][c], qop[c], s[p]);
+      for (int c = 0; c < NDC; ++c) {
+        bf16x8 ka;
+        if constexpr (FP8) {
+          const u32x4 raw = r.k[p][c >> 1];
+          ka = (c & 1) ? e4m3x8_to_bf16(raw[2], raw[3]) : e4m3x8_to_bf16(raw[0], raw[1]);
+        } else {
+          ka = r.k[p][c];
+        }
+        s[p] = mfma_16x16x32(ka, qop[c], s[p]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     issue(r, pid, mp);
@@ -390,7 +466,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k
   PairMeta mb = cur_meta();
   int pidb = load_pid();
   advance();
-  PairRegs<D> ra, rb;
+  PairRegs<D, FP8> ra, rb;
   __builtin_amdgcn_sched_barrier(0);
   issue(ra, pida, ma);
   PairMeta mpa = cur_meta();
@@ -495,16 +571,15 @@ void decode_combine_kernel(const int32_t* __restrict__ seq_lens, const int2* __r
   if (lse != nullptr && lane == 0) lse[nh] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
-template <int D>
+template <int D, bool FP8>
 hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                     const DecodeWorkspace& ws, int N, int Hq, int Hkv, int num_pages,
-                    int max_blocks, float scale_log2, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<D>), dim3(kDecodeWaves), dim3(64), 0, stream,
-                     static_cast<const bf16*>(q), static_cast<const bf16*>(k_pool),
-                     static_cast<const bf16*>(v_pool), block_table, seq_lens,
+                    int max_blocks, float scale_log2, float v_scale, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_stream_kernel<D, FP8>), dim3(kDecodeWaves), dim3(64), 0, stream,
+                     static_cast<const bf16*>(q), k_pool, v_pool, block_table, seq_lens,
                      static_cast<bf16*>(o), lse, ws.seg_waves, ws.o_part, ws.lse_part, N, Hq, Hkv,
-                     num_pages, max_blocks, scale_log2);
+                     num_pages, max_blocks, scale_log2, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(N * Hq), dim3(64), 0, stream, seq_lens,
@@ -519,12 +594,18 @@ hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_
                                const int32_t* block_table, const int32_t* seq_lens, void* o,
                                float* lse, const DecodeWorkspace& ws, int N, int Hq, int Hkv,
                                int d, int num_pages, int max_blocks, float scale_log2,
-                               hipStream_t stream) {
-  if (d == 128)
-    return launch_d<128>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N, Hq, Hkv,
-                         num_pages, max_blocks, scale_log2, stream);
-  return launch_d<64>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N, Hq, Hkv, num_pages,
-                      max_blocks, scale_log2, stream);
+                               bool fp8, float v_scale, hipStream_t stream) {
+  if (fp8)
+    return d == 128 ? launch_d<128, true>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
+                                          Hq, Hkv, num_pages, max_blocks, scale_log2, v_scale,
+                                          stream)
+                    : launch_d<64, true>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
+                                         Hq, Hkv, num_pages, max_blocks, scale_log2, v_scale,
+                                         stream);
+  return d == 128 ? launch_d<128, false>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
+                                         Hq, Hkv, num_pages, max_blocks, scale_log2, 1.f, stream)
+                  : launch_d<64, false>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
+                                        Hq, Hkv, num_pages, max_blocks, scale_log2, 1.f, stream);
 }
 
 }  // namespace attn

@@ -49,11 +49,13 @@ struct DecodeWorkspace {
   float* lse_part;                   // [2 * kDecodeWaves][kDecodeMaxG]
 };
 
+// fp8: pools hold E4M3 codes; scale_log2 then includes the key scale and
+// v_scale multiplies the output (ignored for bf16 pools).
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* seq_lens,
                                void* o, float* lse, const DecodeWorkspace& ws,
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
-                               float scale_log2, hipStream_t stream);
+                               float scale_log2, bool fp8, float v_scale, hipStream_t stream);
 
 // Backward, bf16 in/out, fp32 accumulation on MFMA: the row statistics
 // (LSE * log2 e, D = rowsum(dO * O)) into ws.stats [B*Hq*T][2] floats, then

@@ -35,6 +35,10 @@ v are prefill_3's (same seed), with dO drawn after them.
 ``make_prefill_paged`` lays chunked-prefill inputs out like ``make_decode``;
 ``chunked_prefill_6`` is its benchmark case: 16 sequences with 1024..8192
 cached tokens whose last 512 are the chunk, on the decode model shape.
+``make_decode_fp8`` draws as ``make_decode`` and quantises K and V to E4M3
+codes (value / scale, torch's float8_e4m3fn cast; quantising is input
+preparation, the attention only ever sees the codes and the scales);
+``decode_fp8_7`` is decode_5's shape with such pages.
 """
 from __future__ import annotations
 
@@ -263,6 +267,69 @@ def make_prefill_paged(N, Hq, Hkv, T, d, min_len, max_len, q_lens=None, lens=Non
                               name=name)
 
 
+@dataclass
+class DecodeFp8Inputs:
+    """Paged decode with E4M3 key/value pages (codes as uint8) and per-tensor scales."""
+    N: int
+    Hq: int
+    Hkv: int
+    d: int
+    page: int
+    num_pages: int
+    max_blocks: int
+    scale: float
+    k_scale: float
+    v_scale: float
+    seq_lens: np.ndarray
+    block_table: np.ndarray
+    q: object                   # torch CPU bf16 [N, Hq, d]
+    k_codes: object             # torch CPU uint8 [num_pages, Hkv, page, d]
+    v_codes: object
+    name: str = ""
+
+
+def make_decode_fp8(N, Hq, Hkv, d, min_len, max_len, page=PAGE, max_blocks=None, seed=0,
+                    k_scale=2.0 ** -5, v_scale=2.0 ** -5, poison_tail=False, lens=None, name=""):
+    """The draws of ``make_decode`` (same order and seed use), then K and V
+    quantised to E4M3 codes of value / scale by torch's float8_e4m3fn cast
+    (round to nearest even; |value| / scale stays far below 448 for N(0,1)
+    draws at the default scale 2^-5).  ``poison_tail`` writes the NaN code
+    0x7F into the unused slots of every last page."""
+    import torch
+    rng = np.random.default_rng(seed)
+    drawn = rng.integers(min_len, max_len + 1, N)
+    seq_lens = np.asarray(drawn if lens is None else lens, dtype=np.int64)
+    pages_per = (seq_lens + page - 1) // page
+    if max_blocks is None:
+        max_blocks = int((max_len + page - 1) // page)
+    P = int(pages_per.sum())
+    perm = rng.permutation(P)
+    block_table = np.full((N, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for n in range(N):
+        cnt = int(pages_per[n])
+        block_table[n, :cnt] = perm[off:off + cnt]
+        off += cnt
+    q = rng.standard_normal((N, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+    v = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+
+    def codes(x, sc):
+        return (torch.from_numpy(x / np.float32(sc)).to(torch.float8_e4m3fn)
+                .view(torch.uint8).contiguous())
+    kc, vc = codes(k, k_scale), codes(v, v_scale)
+    if poison_tail:
+        for n in range(N):
+            used = int(seq_lens[n]) - (int(pages_per[n]) - 1) * page
+            if used < page:
+                last = block_table[n, int(pages_per[n]) - 1]
+                kc[last, :, used:, :] = 0x7F
+                vc[last, :, used:, :] = 0x7F
+    return DecodeFp8Inputs(N, Hq, Hkv, d, page, P, max_blocks, 1.0 / math.sqrt(d), float(k_scale),
+                           float(v_scale), seq_lens.astype(np.int32), block_table, _cast(q, "bf16"),
+                           kc, vc, name=name)
+
+
 # --- the five named workloads -------------------------------------------------
 
 def prefill_1():
@@ -294,6 +361,13 @@ def chunked_prefill_6():
                               name="chunked_prefill_6")
 
 
+def decode_fp8_7(poison_tail=False):
+    """decode_5's shape (64 sequences, lengths U[512, 8192], Hq=12, Hkv=2,
+    d=128, 16-token pages) with E4M3 key/value pages."""
+    return make_decode_fp8(64, 12, 2, 128, 512, 8192, page=PAGE, max_blocks=512, seed=1007,
+                           poison_tail=poison_tail, name="decode_fp8_7")
+
+
 def backward_3():
     """The gradient pass of prefill_3 (same q, k, v), dO drawn after v."""
     return make_backward(4, 12, 2, 4096, 4096, 128, causal=True, seed=1003, name="backward_3")
@@ -307,6 +381,7 @@ WORKLOADS = {
     "decode_5": decode_5,
     "backward_3": backward_3,
     "chunked_prefill_6": chunked_prefill_6,
+    "decode_fp8_7": decode_fp8_7,
 }
 
 # Human-readable shapes, used for labels in the benchmark output.
@@ -319,4 +394,6 @@ SHAPES = {
     "backward_3": dict(B=4, Hq=12, Hkv=2, T=4096, S=4096, d=128, dtype="bf16", causal=True),
     "chunked_prefill_6": dict(N=16, Hq=12, Hkv=2, T=512, d=128, page=16, min_len=1024,
                               max_len=8192, dtype="bf16"),
+    "decode_fp8_7": dict(N=64, Hq=12, Hkv=2, d=128, page=16, min_len=512, max_len=8192,
+                         dtype="bf16 q, e4m3 kv"),
 }
