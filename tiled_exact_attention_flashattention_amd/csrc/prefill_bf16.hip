@@ -323,11 +323,19 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // online softmax update (base 2), per row block
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      float mx = -INFINITY;
+      // per key block a 3-input max pair, then a 3-input tree over the blocks
+      float mk[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        mx = fmax2(mx, fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), fmax2(s[qb][kb][2], s[qb][kb][3])));
-      mx = pair_max32(pair_max16(mx));
+        mk[kb] = fmax2(fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), s[qb][kb][2]), s[qb][kb][3]);
+#pragma unroll
+      for (int w = NKB; w > 1; w = (w + 2) / 3)
+#pragma unroll
+        for (int i = 0; i < (w + 2) / 3; ++i) {
+          const float a = mk[3 * i], b = 3 * i + 1 < w ? mk[3 * i + 1] : a, c = 3 * i + 2 < w ? mk[3 * i + 2] : a;
+          mk[i] = fmax2(fmax2(a, b), c);
+        }
+      float mx = pair_max32(pair_max16(mk[0]));
       // The reference maximum only moves when the tile's maximum exceeds it
       // by more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau
       // and the accumulator is rarely rescaled; any reference gives the same
