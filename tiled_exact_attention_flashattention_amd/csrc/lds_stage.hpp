@@ -61,15 +61,16 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // 16-byte-chunk swizzle for a row-major [rows][D] bf16 tile that is read both
-// ways: as MFMA row operands (16 consecutive rows, one chunk each) and through
-// the LDS transpose read (8 consecutive rows, one 32-byte chunk pair each).
-// The first needs 16 consecutive rows on distinct chunks (per row parity at
-// D=64, whose rows are half a bank line); the second needs the pair index
-// swz >> 1 distinct over 8 consecutive rows.  Both hold for these forms
-// (checked bank by bank on the CPU).
+// ways: as MFMA row operands (16 consecutive rows, one chunk each, by
+// ds_read_b128) and through the LDS transpose read (8 consecutive rows, one
+// 32-byte chunk pair each).  Measured on gfx950 with SQ_LDS_BANK_CONFLICT
+// for both read patterns of the kernels that use it: this form (the chunk
+// pair index from the row, D = 64 rows being half a bank line) reads both
+// ways without conflicts; adding row bit 3 into chunk bit 0 made every
+// ds_read_b128 of the pattern pay about four conflict cycles.
 template <int D>
 __device__ __forceinline__ int dual_swz(int row) {
-  return D == 128 ? 2 * (row & 7) + ((row >> 3) & 1) : 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+  return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3);
 }
 
 }  // namespace attn
