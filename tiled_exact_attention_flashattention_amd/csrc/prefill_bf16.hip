@@ -73,6 +73,9 @@ __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 
+// Chunked prefill: sequences are ranked by length on the device up to this count.
+constexpr int kSortMax = 256;
+
 // Slack of the running maximum (log2 units): P = exp2(s - m) may reach
 // 2^kLazyTau, far inside bf16 and fp32 range.
 constexpr float kLazyTau = 8.f;
@@ -112,7 +115,33 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int G = B * Hkv;                     // (batch, KV head) groups
   const int pid = blockIdx.x;
   int hgi, grp, rank;
-  if ((G & 7) == 0) {
+  if (PAGED) {
+    // Chunked prefill: a sequence's work grows with its cached length, so
+    // sequences are dispatched longest first (workgroups [slot W, (slot+1) W)
+    // take the slot-th longest, ties by index; with more than kSortMax
+    // sequences the given order is kept).  Every workgroup ranks the same
+    // lengths, so all agree on the order.
+    const int W = ntq * Hq, slot = pid / W, w = pid - slot * W;
+    hgi = w % hpg;
+    const int r = w / hpg;
+    rank = r / Hkv;
+    int bsel = slot;
+    if (B <= kSortMax) {
+      __shared__ int sel;
+      for (int cand = threadIdx.x; cand < B; cand += kThreads) {
+        const int lc = pkv.seq_lens[cand];
+        int rk = 0;
+        for (int t = 0; t < B; ++t) {
+          const int lt = pkv.seq_lens[t];
+          rk += (lt > lc) || (lt == lc && t < cand);
+        }
+        if (rk == slot) sel = cand;
+      }
+      __syncthreads();
+      bsel = sel;
+    }
+    grp = bsel * Hkv + r % Hkv;
+  } else if ((G & 7) == 0) {
     // XCD pid%8 walks its own eighth of the groups: [tile rank][group][head].
     int s = pid >> 3;
     const int gpx = G >> 3;
