@@ -101,6 +101,28 @@ __device__ __forceinline__ float pair_sum32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Maximum of three floats, one v_max3_f32.  Written out because fmaxf first
+// quiets signalling NaNs in every operand that the compiler cannot prove
+// canonical (one v_max per operand, twice the work); the operands here are
+// MFMA results or their maxima, finite or -inf.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// pair_max16 / pair_max32 on max3_raw.
+__device__ __forceinline__ float pair_max16_raw(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_max32_raw(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
+}
+
 // True in every lane if the predicate holds in any lane of the wave.
 __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballot_w64(p) != 0; }
 

@@ -352,19 +352,24 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // online softmax update (base 2), per row block
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // per key block a 3-input max pair, then a 3-input tree over the blocks
-      float mk[NKB];
+      // row maximum of the tile: a three-input max tree over its 4 NKB scores
+      float mk[4 * NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        mk[kb] = fmax2(fmax2(fmax2(s[qb][kb][0], s[qb][kb][1]), s[qb][kb][2]), s[qb][kb][3]);
 #pragma unroll
-      for (int w = NKB; w > 1; w = (w + 2) / 3)
+        for (int i = 0; i < 4; ++i) mk[4 * kb + i] = s[qb][kb][i];
+#pragma unroll
+      for (int w = 4 * NKB; w > 1; w = (w + 2) / 3)
 #pragma unroll
         for (int i = 0; i < (w + 2) / 3; ++i) {
-          const float a = mk[3 * i], b = 3 * i + 1 < w ? mk[3 * i + 1] : a, c = 3 * i + 2 < w ? mk[3 * i + 2] : a;
-          mk[i] = fmax2(fmax2(a, b), c);
+          if (3 * i + 1 == w) {                      // a lone last value moves up as is
+            mk[i] = mk[3 * i];
+          } else {
+            const float a = mk[3 * i], b = mk[3 * i + 1], c = 3 * i + 2 < w ? mk[3 * i + 2] : b;
+            mk[i] = max3_raw(a, b, c);
+          }
         }
-      float mx = pair_max32(pair_max16(mk[0]));
+      float mx = pair_max32_raw(pair_max16_raw(mk[0]));
       // The reference maximum only moves when the tile's maximum exceeds it
       // by more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau
       // and the accumulator is rarely rescaled; any reference gives the same
