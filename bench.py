@@ -307,7 +307,8 @@ def write_counters(pmc_dir):
            "commands": {"copy": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
                                 "-- python3 bench.py --copy-probe",
                         "bench": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
-                                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-flush --no-other-prefill"}}
+                                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-flush --no-other-prefill "
+                                 "--no-backward --no-next"}}
     for kind, pattern in (("prefill", ["prefill_bf16_kernel"]),
                           ("decode", ["decode_stream_kernel", "decode_combine_kernel"])):
         t = bytes_of(pattern)
