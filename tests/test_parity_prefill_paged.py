@@ -5,9 +5,12 @@ Small cases cover ragged chunk and context lengths, chunks that fill the
 whole context, one-token chunks, the sliding window, poisoned (NaN) slots
 past each sequence's end, GQA ratios and both head sizes; a chunk equal to
 the whole sequence must reproduce attn_fwd on the contiguous keys bit for
-bit.  The full-size chunked workload (16 sequences, 512-token chunks, up to
-8192 cached tokens) is compared on sampled rows in the configuration the
-benchmark times.
+bit.  Sequences are dispatched longest first by a rank the kernel computes
+from the lengths (up to 256 sequences, ties by index, in the given order
+above that): equal lengths and more than 256 sequences must still give every
+sequence its own workgroups.  The full-size chunked workload (16 sequences,
+512-token chunks, up to 8192 cached tokens) is compared on sampled rows in
+the configuration the benchmark times.
 """
 import numpy as np
 import pytest
@@ -36,8 +39,13 @@ def _run(inp):
 
 
 def _check(inp, name, o, lse, seqs=None, rows_of=None):
+    """Every computed row against the oracle: the maximum errors element by
+    element, the mean error of O over all the rows checked (the bf16 bound is
+    a mean over the output, which a single short row, its values rounded once
+    to bf16, can exceed on its own)."""
     q, kp, vp = inp.f64()
     seqs = range(inp.N) if seqs is None else seqs
+    got_o, ref_o = [], []
     for n in seqs:
         L, Tn = int(inp.seq_lens[n]), int(inp.q_lens[n])
         rows = np.arange(Tn) if rows_of is None else rows_of(n, Tn)
@@ -47,10 +55,12 @@ def _check(inp, name, o, lse, seqs=None, rows_of=None):
             for h in range(hk * (inp.Hq // inp.Hkv), (hk + 1) * (inp.Hq // inp.Hkv)):
                 o_ref, l_ref = oracle.attention_head(q[n, h, :Tn], kn, vn, inp.scale, True, rows,
                                                      window=inp.window)
-                check_o(to_np(o[n, h, rows]), o_ref, "bf16", f"{name} n={n} h={h}")
+                got_o.append(to_np(o[n, h, rows]).reshape(-1))
+                ref_o.append(np.asarray(o_ref).reshape(-1))
                 check_lse(to_np(lse[n, h, rows]), l_ref, f"{name} n={n} h={h}")
         if rows_of is None:
             assert bool((o[n, :, Tn:] == 7.0).all()) and bool((lse[n, :, Tn:] == 7.0).all())
+    check_o(np.concatenate(got_o), np.concatenate(ref_o), "bf16", name)
 
 
 # name, N, Hq, Hkv, T, d, min_len, max_len, q_lens, window, poison
@@ -101,6 +111,27 @@ def test_whole_sequence_chunk_is_bitwise_attn_fwd(d):
                      for n in range(inp.N)]).cuda().contiguous()
     o_f, l_f = tea.fwd(inp.q.cuda(), k, v, scale=inp.scale, causal=True)
     assert torch.equal(o, o_f) and torch.equal(lse, l_f)
+
+
+def test_equal_lengths_each_sequence_computed_once():
+    name = "pp_ties"
+    lens = [300, 300, 120, 300, 120, 57, 300]
+    qls = [40, 40, 40, 1, 120, 57, 33]
+    inp = workloads.make_prefill_paged(7, 4, 2, 120, 128, 0, 0, q_lens=qls, lens=lens,
+                                       seed=seed_of(name), poison_tail=True, extra_pages=2,
+                                       name=name)
+    announce(f"attn_prefill_paged {name}: seq_lens={lens} q_lens={qls}")
+    o, lse = _run(inp)
+    _check(inp, name, o, lse)
+
+
+def test_more_sequences_than_the_device_ranking_covers():
+    name = "pp_many"
+    inp = workloads.make_prefill_paged(300, 2, 1, 8, 64, 1, 64, seed=seed_of(name),
+                                       poison_tail=True, extra_pages=3, name=name)
+    announce(f"attn_prefill_paged {name}: N=300 Hq=2 Hkv=1 T=8 d=64")
+    o, lse = _run(inp)
+    _check(inp, name, o, lse)
 
 
 def test_chunked_prefill_6_sampled():
