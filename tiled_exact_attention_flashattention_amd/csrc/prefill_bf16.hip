@@ -45,22 +45,28 @@
 #define PREFILL_D128_BN 64
 #define PREFILL_D128_STAGES 2
 #define PREFILL_D64_WAVES 4
-#define PREFILL_D64_BN 128
+#define PREFILL_D64_BN_QB1 128
+#define PREFILL_D64_BN_QB2 64
 #define PREFILL_D64_STAGES 2
 #endif
 
 namespace attn {
 namespace {
 
-// Tile configuration per head dimension: waves per workgroup (32 query rows
-// each), keys per K/V tile, and LDS stages in the load ring (the load of tile
-// j + STAGES - 1 is in flight while tile j is computed).
-template <int D> struct PrefillCfg;
-template <> struct PrefillCfg<128> {
+// Tile configuration per head dimension and row blocks per wave (QB): waves
+// per workgroup (16 QB query rows each), keys per K/V tile, and LDS stages in
+// the load ring (the load of tile j + STAGES - 1 is in flight while tile j is
+// computed).  At d = 64 one row block per wave serves the small grids, whose
+// time is the longest workgroup's path, and takes 128-key tiles (half the
+// steps on that path); two row blocks per wave serve full grids with 64-key
+// tiles, which measured 5-8 % faster there than 128 (prefill_2, same-box A/B).
+template <int D, int QB> struct PrefillCfg;
+template <int QB> struct PrefillCfg<128, QB> {
   static constexpr int WAVES = PREFILL_D128_WAVES, BN = PREFILL_D128_BN, STAGES = PREFILL_D128_STAGES;
 };
-template <> struct PrefillCfg<64> {
-  static constexpr int WAVES = PREFILL_D64_WAVES, BN = PREFILL_D64_BN, STAGES = PREFILL_D64_STAGES;
+template <int QB> struct PrefillCfg<64, QB> {
+  static constexpr int WAVES = PREFILL_D64_WAVES, STAGES = PREFILL_D64_STAGES;
+  static constexpr int BN = QB == 1 ? PREFILL_D64_BN_QB1 : PREFILL_D64_BN_QB2;
 };
 
 // Chunk swizzles (16-byte chunks within a row of D bf16).
@@ -81,16 +87,16 @@ constexpr int kSortMax = 256;
 constexpr float kLazyTau = 8.f;
 
 template <int D, bool CAUSAL, int QB, bool PAGED>
-__global__ __launch_bounds__(64 * PrefillCfg<D>::WAVES) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__((64 * PrefillCfg<D, QB>::WAVES)) __attribute__((amdgpu_waves_per_eu(2)))
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
                          float scale_log2, int window, const PagedKv pkv) {
-  constexpr int BN = PrefillCfg<D>::BN;
-  constexpr int NST = PrefillCfg<D>::STAGES;
-  constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
+  constexpr int BN = PrefillCfg<D, QB>::BN;
+  constexpr int NST = PrefillCfg<D, QB>::STAGES;
+  constexpr int kThreads = 64 * PrefillCfg<D, QB>::WAVES;
   constexpr int kWR = 16 * QB;               // query rows per wave (QB blocks of 16)
-  constexpr int kBM = kWR * PrefillCfg<D>::WAVES;  // query rows per workgroup
+  constexpr int kBM = kWR * PrefillCfg<D, QB>::WAVES;  // query rows per workgroup
   constexpr int CPR = D / 8;                 // 16-byte chunks per row
   constexpr int NKB = BN / 16;               // 16-key blocks of S^T
   constexpr int NDC = D / 32;                // k-chunks of the S^T MFMA
@@ -224,13 +230,13 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   static_assert(!PAGED || NST == 2, "the page-id stream assumes a two-stage ring");
   constexpr int kRowsPerLoad = 64 / CPR;
   constexpr int kIds = BN / 16;
-  __shared__ int32_t pg_ids[PAGED ? 2 * PrefillCfg<D>::WAVES * 8 : 1];   // [slot][wave][id]
+  __shared__ int32_t pg_ids[PAGED ? 2 * PrefillCfg<D, QB>::WAVES * 8 : 1];   // [slot][wave][id]
   const void* bt_row = PAGED ? uniform_ptr(pkv.block_table + (size_t)b * pkv.max_blocks) : nullptr;
   auto fetch_pages = [&](int j) {
     if (PAGED && lane < kIds) {
       const int blk = min(j * kIds + lane, ((S + 15) >> 4) - 1);
       lds_dma4(uniform_ptr(bt_row), (uint32_t)blk * 4u,
-               lds_addr(pg_ids) + (uint32_t)(((j & 1) * PrefillCfg<D>::WAVES + wave_s) * 32));
+               lds_addr(pg_ids) + (uint32_t)(((j & 1) * PrefillCfg<D, QB>::WAVES + wave_s) * 32));
     }
   };
   auto load_tile = [&](int j, bf16* ks, bf16* vs) {
@@ -238,7 +244,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t vl = lds_addr(vs) + (uint32_t)(wave_s * CPW) * 1024u;
     const bool full = (j + 1) * BN <= S;
     if (PAGED) {
-      const int32_t* ids = pg_ids + ((j & 1) * PrefillCfg<D>::WAVES + wave) * 8;
+      const int32_t* ids = pg_ids + ((j & 1) * PrefillCfg<D, QB>::WAVES + wave) * 8;
 #pragma unroll
       for (int r = 0; r < CPW; ++r) {
         const int key0 = min(j * BN + (wave_s * CPW + r) * kRowsPerLoad, S - 1);
@@ -493,8 +499,8 @@ template <int D, bool CAUSAL, int QB, bool PAGED>
 hipError_t launch_one(const void* q, const void* k, const void* v, void* o, float* lse,
                       int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
                       const PagedKv& pkv, hipStream_t stream) {
-  constexpr int kThreads = 64 * PrefillCfg<D>::WAVES;
-  constexpr int kBM = 16 * QB * PrefillCfg<D>::WAVES;
+  constexpr int kThreads = 64 * PrefillCfg<D, QB>::WAVES;
+  constexpr int kBM = 16 * QB * PrefillCfg<D, QB>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB, PAGED>), dim3((unsigned)grid),
@@ -509,12 +515,13 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
 // query tile) at the price of twice the LDS reads per MFMA.  A grid of at
 // most one workgroup per CU is bound by that path (B=1 at T=1024, d=64: 11 us
 // instead of 16 us), so it gets one block per wave; a fuller grid is bound by
-// the total work (B=8 at the same shape: 30 us instead of 28.5 us).
+// the total work (B=8 at the same shape, 128-key tiles: 30 us instead of
+// 28.5 us).
 template <int D, bool CAUSAL, bool PAGED = false>
 hipError_t launch_rows(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int Hq, int Hkv, int T, int S, float scale_log2, int window,
                        hipStream_t stream, const PagedKv& pkv = PagedKv{}) {
-  constexpr int kBM2 = 32 * PrefillCfg<D>::WAVES;
+  constexpr int kBM2 = 32 * PrefillCfg<D, 2>::WAVES;
   const long long wgs2 = (long long)((T + kBM2 - 1) / kBM2) * B * Hq;
   if (wgs2 < PREFILL_SMALL_GRID)
     return launch_one<D, CAUSAL, 1, PAGED>(q, k, v, o, lse, B, Hq, Hkv, T, S, scale_log2, window,
