@@ -79,6 +79,11 @@ __device__ __forceinline__ int k_swz(int row) { return D == 128 ? (row & 15) : (
 template <int D>
 __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) : 2 * ((row >> 1) & 3); }
 
+// MI355X: 8 XCDs of 32 CUs; the dispatcher deals workgroups to XCDs in turn
+// and, inside an XCD, to its CUs in turn.
+constexpr int kXcdCount = 8;
+constexpr int kCusPerXcd = 32;
+
 // Chunked prefill: sequences are ranked by length on the device up to this count.
 constexpr int kSortMax = 256;
 
@@ -91,7 +96,7 @@ __global__ __launch_bounds__((64 * PrefillCfg<D, QB>::WAVES)) __attribute__((amd
 void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                          const bf16* __restrict__ v, bf16* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int T, int S,
-                         float scale_log2, int window, const PagedKv pkv) {
+                         float scale_log2, int window, const PagedKv pkv, int snake) {
   constexpr int BN = PrefillCfg<D, QB>::BN;
   constexpr int NST = PrefillCfg<D, QB>::STAGES;
   constexpr int kThreads = 64 * PrefillCfg<D, QB>::WAVES;
@@ -151,6 +156,14 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // XCD pid%8 walks its own eighth of the groups: [tile rank][group][head].
     int s = pid >> 3;
     const int gpx = G >> 3;
+    if (snake) {
+      // The dispatcher deals an XCD's workgroups to its 32 CUs in turn, so
+      // workgroups s, s+32, s+64, ... share a CU.  When the whole grid is
+      // resident at once, taking every other run of 32 in reverse pairs the
+      // heaviest causal tiles with the lightest on each CU.
+      const int run = s >> 5, pos = s & 31;
+      s = (run << 5) + ((run & 1) ? 31 - pos : pos);
+    }
     hgi = s % hpg;
     s /= hpg;
     grp = (pid & 7) * gpx + s % gpx;
@@ -503,10 +516,24 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   constexpr int kBM = 16 * QB * PrefillCfg<D, QB>::WAVES;
   const long long ntq = (T + kBM - 1) / kBM;
   const long long grid = ntq * B * Hq;
+  // Snake order (see the kernel) when the grid is resident all at once and
+  // every XCD's share is whole runs of 32 workgroups.
+  static const int per_cu = [] {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, reinterpret_cast<const void*>(prefill_bf16_kernel<D, CAUSAL, QB, PAGED>), kThreads,
+            0) != hipSuccess)
+      n = 0;
+    return n;
+  }();
+  int snake = 0;
+  if (CAUSAL && !PAGED && ((B * Hkv) & 7) == 0 && grid % 256 == 0 &&
+      grid <= (long long)per_cu * kXcdCount * kCusPerXcd)
+    snake = 1;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB, PAGED>), dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v),
-                     static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S, scale_log2, window, pkv);
+                     static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S, scale_log2, window, pkv, snake);
   return hipGetLastError();
 }
 
