@@ -32,7 +32,8 @@
 //     diagonal (or the ragged end) pay for the mask;
 //   * heavy causal tiles are dispatched first, and when the number of
 //     (batch, KV head) groups is a multiple of 8 every group stays on one XCD
-//     so its K/V is re-read from that XCD's L2.
+//     so its K/V is re-read from that XCD's L2; a grid resident all at once
+//     pairs long and short query tiles on each CU instead.
 #include "cdna4.hpp"
 #include "kernels.hpp"
 #include "lds_stage.hpp"
