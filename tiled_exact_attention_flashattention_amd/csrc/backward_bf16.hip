@@ -211,17 +211,29 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           dp[1][kk] = mfma_16x16x32(vop, dop[1][dc], dp[1][kk]);
         }
       }
-      // dS^T = P^T * (dP^T - D), P^T = exp2(scale_log2 s - LSE2) on visible keys
+      // dS^T = P^T * (dP^T - D), P^T = exp2(scale_log2 s - LSE2), then zero
+      // on keys a row cannot see (only tiles that need it: a select folded
+      // into the loop above would cost two VALU instructions per score on
+      // every tile; the hidden keys' dP is finite, so zeroing the product is
+      // the same as zeroing P)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float p = exp2_hw(__builtin_fmaf(s[qb][kk][i], scale_log2, -lse2[qb]));
-            if (need_mask && j * BN + 32 * c + 16 * kk + 4 * g + i > row_lim[qb]) p = 0.f;
+            const float p = exp2_hw(__builtin_fmaf(s[qb][kk][i], scale_log2, -lse2[qb]));
             s[qb][kk][i] = p * (dp[qb][kk][i] - dd[qb]);
           }
+      if (need_mask) {
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (j * BN + 32 * c + 16 * kk + 4 * g + i > row_lim[qb]) s[qb][kk][i] = 0.f;
+      }
       // dQ^T[d][row] += K^T[d][key] dS^T[key][row] over these 32 keys
       bf16x8 dsop[2];
 #pragma unroll
