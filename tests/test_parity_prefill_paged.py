@@ -73,6 +73,9 @@ CASES = [
     ("pp_window", 4, 8, 2, 200, 128, 200, 900, None, 77, True),
     ("pp_window_d64", 3, 4, 2, 300, 64, 300, 600, 300, 128, False),
     ("pp_medium_gqa", 8, 12, 2, 512, 128, 512, 3000, 512, 0, True),
+    # 256 workgroups: the two-row-block kernel (64-key tiles at d = 64)
+    ("pp_d64_full_grid", 8, 16, 2, 256, 64, 256, 700, None, 0, True),
+    ("pp_d64_full_grid_window", 8, 16, 2, 256, 64, 256, 700, 256, 90, True),
 ]
 
 
