@@ -249,6 +249,47 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: f
     _check(st)
 
 
+def check_paged_inputs(block_table, seq_lens, num_pages: int, page: int = PAGE,
+                       q_lens=None, T: Optional[int] = None) -> None:
+    """Host-side check of what the paged entry points take on trust.
+
+    The kernels read the block table and the lengths on the device, so the C
+    ABI cannot validate them: every page id a sequence uses (block b <
+    ceil(seq_len / page)) must lie in [0, num_pages), every length in
+    [0, max_blocks * page], and for chunked prefill 0 <= q_len <= min(T,
+    seq_len).  (The kernels still never read outside the pools: a bad page id
+    is masked in decode and clamped in prefill, so only that sequence's
+    result is wrong.)  This copies the tensors to the host; it is a debugging
+    aid for callers, not part of any launch.  Raises ValueError naming the
+    first offending sequence.
+    """
+    import numpy as np
+
+    def host(t):
+        return np.asarray(t.detach().cpu().numpy() if hasattr(t, "detach") else t)
+
+    bt, sl = host(block_table), host(seq_lens)
+    if bt.ndim != 2 or sl.ndim != 1 or sl.shape[0] != bt.shape[0]:
+        raise ValueError("block_table must be [N, max_blocks] and seq_lens [N]")
+    max_blocks = bt.shape[1]
+    for n, L in enumerate(sl.tolist()):
+        if L < 0 or L > max_blocks * page:
+            raise ValueError(f"sequence {n}: seq_len {L} outside [0, {max_blocks * page}]")
+        used = bt[n, :(L + page - 1) // page]
+        bad = np.flatnonzero((used < 0) | (used >= num_pages))
+        if bad.size:
+            raise ValueError(f"sequence {n}: block {int(bad[0])} holds page id {int(used[bad[0]])}"
+                             f" outside [0, {num_pages})")
+    if q_lens is not None:
+        ql = host(q_lens)
+        if ql.shape != sl.shape:
+            raise ValueError("q_lens must be [N]")
+        for n, (Tn, L) in enumerate(zip(ql.tolist(), sl.tolist())):
+            hi = L if T is None else min(T, L)
+            if Tn < 0 or Tn > hi:
+                raise ValueError(f"sequence {n}: q_len {Tn} outside [0, {hi}]")
+
+
 def attn_prefill_paged(q, k_pool, v_pool, block_table, seq_lens, q_lens, o, lse, scale: float,
                        window: int = 0, page: int = PAGE, stream=None) -> None:
     """Enqueue attn_prefill_paged on ``stream``.
