@@ -398,18 +398,21 @@ void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ k
     advance();
     __builtin_amdgcn_sched_barrier(0);
 
-    // mask positions past the length and masked pages
+    // mask positions past the length and masked pages (only a segment's last
+    // pair, or a pair with a masked page, has any)
+    if (m.tv0 < kPage || m.tv1 < kPage) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const int tv = p ? m.tv1 : m.tv0;
+      for (int p = 0; p < 2; ++p) {
+        const int tv = p ? m.tv1 : m.tv0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * g + i >= tv) s[p][i] = -INFINITY;
+        for (int i = 0; i < 4; ++i)
+          if (4 * g + i >= tv) s[p][i] = -INFINITY;
+      }
     }
 
-    float mx = fmax2(fmax2(fmax2(s[0][0], s[0][1]), fmax2(s[0][2], s[0][3])),
-                     fmax2(fmax2(s[1][0], s[1][1]), fmax2(s[1][2], s[1][3])));
-    mx = pair_max32(pair_max16(mx));
+    float mx = max3_raw(max3_raw(s[0][0], s[0][1], s[0][2]), max3_raw(s[0][3], s[1][0], s[1][1]),
+                        max3_raw(s[1][2], s[1][3], s[1][3]));
+    mx = pair_max32_raw(pair_max16_raw(mx));
     const float m_new = fmax2(m_run, mx * scale_log2);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_hw(m_run - m_use);
