@@ -133,7 +133,16 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // take the slot-th longest, ties by index; with more than kSortMax
     // sequences the given order is kept).  Every workgroup ranks the same
     // lengths, so all agree on the order.
-    const int W = ntq * Hq, slot = pid / W, w = pid - slot * W;
+    // The first two rounds of the dispatch put workgroups pid and pid + 256
+    // on one CU (the first 512 ids fill two slots of each of the 256 CUs):
+    // ids 256..511 take the lightest items, in reverse, so that each CU
+    // starts with one long and one short query tile; later ids take the
+    // middle of the order, longest first.
+    const int G_all = (int)gridDim.x, nc = kXcdCount * kCusPerXcd;
+    int item = pid;
+    if (pid >= nc && pid < 2 * nc) item = G_all - 1 - (pid - nc);
+    else if (pid >= 2 * nc) item = pid - nc;
+    const int W = ntq * Hq, slot = item / W, w = item - slot * W;
     hgi = w % hpg;
     const int r = w / hpg;
     rank = r / Hkv;
