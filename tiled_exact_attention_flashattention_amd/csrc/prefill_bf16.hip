@@ -316,10 +316,12 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
   // ---- running softmax state of rows wrow0 + 16 qb + l16 ----
   float m_run[QB], l_part[QB];               // running max of scaled logits (log2 units);
+  float m_use[QB];                           // m_run, or 0 while it is -inf (exponent offset)
   f32x4 acc[QB][NDB];                        // sum over this lane's keys of exp2(s - m_run)
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     m_run[qb] = -INFINITY;
+    m_use[qb] = 0.f;
     l_part[qb] = 0.f;
   }
 #pragma unroll
@@ -398,34 +400,38 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             mk[i] = max3_raw(a, b, c);
           }
         }
-      float mx = pair_max32_raw(pair_max16_raw(mk[0]));
       // The reference maximum only moves when the tile's maximum exceeds it
       // by more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau
       // and the accumulator is rarely rescaled; any reference gives the same
       // O and LSE (it cancels between acc and l), only the rounding changes.
-      const float m_tile = mx * scale_log2;
-      const bool grow = m_tile > m_run[qb] + kLazyTau;   // always when m_run = -inf
-      const float m_new = grow ? m_tile : m_run[qb];
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run[qb] - m_use);
-      const bool rescale = wave_any(grow);
-      m_run[qb] = m_new;
-      float rs = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -m_use));
-          s[qb][kb][i] = p;
-          rs += p;
-        }
-      l_part[qb] = __builtin_fmaf(l_part[qb], alpha, rs);
-      if (rescale) {
+      // A row's maximum can only pass that bar if one of its four lanes' own
+      // maxima does (scale > 0), so the cross-lane maximum, the new
+      // reference and the rescale factor are only formed on tiles where some
+      // lane of the wave passes it; elsewhere nothing moves and alpha is 1.
+      float alpha = 1.f;
+      if (wave_any(mk[0] * scale_log2 > m_run[qb] + kLazyTau)) {   // always when m_run = -inf
+        const float m_tile = pair_max32_raw(pair_max16_raw(mk[0])) * scale_log2;
+        const bool grow = m_tile > m_run[qb] + kLazyTau;
+        const float m_new = grow ? m_tile : m_run[qb];
+        const float m_off = (m_new == -INFINITY) ? 0.f : m_new;
+        alpha = exp2_hw(m_run[qb] - m_off);
+        m_run[qb] = m_new;
+        m_use[qb] = m_off;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha;
       }
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -m_use[qb]));
+          s[qb][kb][i] = p;
+          rs += p;
+        }
+      l_part[qb] = __builtin_fmaf(l_part[qb], alpha, rs);
     }
 
     // O^T += V^T P^T, 32 keys at a time; each V operand feeds both row blocks
