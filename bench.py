@@ -62,9 +62,12 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = {
     "prefill": ["tiled_exact_attention_flashattention_amd/csrc/prefill_bf16.hip",
-                "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp"],
+                "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp",
+                "tiled_exact_attention_flashattention_amd/csrc/lds_stage.hpp",
+                "tiled_exact_attention_flashattention_amd/csrc/kernels.hpp"],
     "decode": ["tiled_exact_attention_flashattention_amd/csrc/decode_paged.hip",
-               "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp"],
+               "tiled_exact_attention_flashattention_amd/csrc/cdna4.hpp",
+               "tiled_exact_attention_flashattention_amd/csrc/kernels.hpp"],
 }
 
 

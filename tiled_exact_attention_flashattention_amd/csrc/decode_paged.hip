@@ -14,7 +14,7 @@
 // Work distribution.  The unit of work is a page pair (32 keys) of one
 // (sequence, KV head) segment; units are numbered sequence-major, then KV
 // head, then pair.  A persistent grid of kDecodeWaves single-wave workgroups
-// (8 per CU on 256 CUs) splits the U units into equal contiguous ranges, so
+// (4 per CU on 256 CUs) splits the U units into equal contiguous ranges, so
 // every CU carries the same load: the kernel is bound by HBM and a CU's share
 // of the bandwidth grows with the waves it holds, so an uneven spread of
 // waves over CUs, not the bytes in flight, is what a fixed split size loses.
@@ -50,6 +50,9 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 constexpr int kPage = 16;
 constexpr int kMinPairsPerWave = 4;   // fewer units than 4 per wave: use fewer waves
+#ifndef DECODE_COMBINE_CH
+#define DECODE_COMBINE_CH 16       // pieces whose partials one combine wave loads at a time
+#endif
 
 __device__ __forceinline__ int wave_sum(int x) {
 #pragma unroll
@@ -507,7 +510,7 @@ void decode_combine_kernel(const int32_t* __restrict__ seq_lens, const int2* __r
                            bf16* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv,
                            int max_blocks) {
   constexpr int PER = D / 64;
-  constexpr int CH = 16;
+  constexpr int CH = DECODE_COMBINE_CH;
   const int nh = blockIdx.x;
   const int n = nh / Hq, h = nh - n * Hq;
   const int G = Hq / Hkv, hk = h / G, hh = h - hk * G;
