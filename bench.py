@@ -29,6 +29,8 @@ Reported (one JSON line on stdout):
   decode_fp8     attn_decode_paged_fp8 on decode_5's shape with E4M3 pages
                  (decode_fp8_7): GB/s over the bytes it must read (one byte
                  per cached K/V element, plus q, o, lse, lengths, block table);
+  (window, chunked and decode_fp8 each carry their own cpu_baseline: the
+  oracle timed on sampled heads or sequences of the same workload)
   backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
                  kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
                  T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
@@ -108,6 +110,18 @@ def blas_threads():
         return 1
 
 
+def oracle_sample(budget_s, units, run_unit, work_of):
+    """Run the oracle on units[0], units[1], ... (cycling) until budget_s seconds
+    are spent; returns (units done, algorithmic work done, seconds)."""
+    done, work, t0 = 0, 0, time.perf_counter()
+    while time.perf_counter() - t0 < budget_s:
+        u = units[done % len(units)]
+        run_unit(u)
+        work += work_of(u)
+        done += 1
+    return done, work, time.perf_counter() - t0
+
+
 def cpu_baseline(pinp, dinp, budget_s):
     """Time the oracle on a bounded sample of both workloads (host cores).
 
@@ -166,8 +180,8 @@ def timed_launches(stream, flush, launch, n=7, skip=2):
     return sum(a.elapsed_time(b_) for a, b_ in times) / len(times), len(times)
 
 
-def bench_window(tea, workloads, dev, stream, flush, window=1024):
-    """attn_fwd_window on the GQA causal workload."""
+def bench_window(tea, workloads, dev, stream, flush, cpu_budget_s=None, window=1024):
+    """attn_fwd_window on the GQA causal workload (and the oracle on sampled heads)."""
     import torch
     x = workloads.prefill_3()
     xq, xk, xv = (t.to(dev) for t in (x.q, x.k, x.v))
@@ -177,14 +191,32 @@ def bench_window(tea, workloads, dev, stream, flush, window=1024):
         xq, xk, xv, xo, xl, x.scale, window, stream=stream))
     fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, True, 2, window=window)
     tf = fl / (ms * 1e-3) / 1e12
-    return {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal, "
-                      f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms, "value": tf,
-            "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
-            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
+    rec = {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal, "
+                     f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms, "value": tf,
+           "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
+           "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n,
+           "cpu_baseline": None}
+    del xq, xk, xv, xo, xl
+    if cpu_budget_s:
+        import oracle
+        g = x.Hq // x.Hkv
+        heads = [(b, h) for b in range(x.B) for h in range(x.Hq)]
+        done, work, tc = oracle_sample(
+            cpu_budget_s, heads,
+            lambda bh: oracle.attention_head(x.q[bh[0], bh[1]].double().numpy(),
+                                             x.k[bh[0], bh[1] // g].double().numpy(),
+                                             x.v[bh[0], bh[1] // g].double().numpy(),
+                                             x.scale, True, window=window),
+            lambda bh: fl // len(heads))
+        rec["cpu_baseline"] = {"value": work / tc / 1e12, "unit": "TFLOP/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{done} (batch, head) windowed attention problems of "
+                                         f"this workload ({tc:.1f} s)"}
+    return rec
 
 
-def bench_chunked(tea, workloads, dev, stream, flush):
-    """attn_prefill_paged on chunked_prefill_6."""
+def bench_chunked(tea, workloads, dev, stream, flush, cpu_budget_s=None):
+    """attn_prefill_paged on chunked_prefill_6 (and the oracle on sampled sequences)."""
     import torch
     x = workloads.chunked_prefill_6()
     xq, kp, vp = (t.to(dev) for t in (x.q, x.k_pool, x.v_pool))
@@ -197,15 +229,32 @@ def bench_chunked(tea, workloads, dev, stream, flush):
                 for L, T in zip(x.seq_lens, x.q_lens))   # row i sees L - T + i + 1 keys
     fl = 4 * x.d * x.Hq * pairs
     tf = fl / (ms * 1e-3) / 1e12
-    return {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, chunk {x.T}, cached "
-                      f"{int(x.seq_lens.min())}..{int(x.seq_lens.max())} tokens, d={x.d}, bf16, "
-                      f"16-token pages", "kernel": "prefill_bf16_kernel (paged)", "ms": ms,
-            "value": tf, "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
-            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n}
+    rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, chunk {x.T}, cached "
+                     f"{int(x.seq_lens.min())}..{int(x.seq_lens.max())} tokens, d={x.d}, bf16, "
+                     f"16-token pages", "kernel": "prefill_bf16_kernel (paged)", "ms": ms,
+           "value": tf, "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
+           "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n,
+           "cpu_baseline": None}
+    del xq, kp, vp, bt, sl, ql, xo, xl
+    if cpu_budget_s:
+        import oracle
+        qd, kd, vd = x.f64()
+        done, work, tc = oracle_sample(
+            cpu_budget_s, list(range(x.N)),
+            lambda n: oracle.prefill_paged(qd[n:n + 1], kd, vd, x.block_table[n:n + 1],
+                                           x.seq_lens[n:n + 1], x.q_lens[n:n + 1], x.scale),
+            lambda n: 4 * x.d * x.Hq * (int(x.seq_lens[n]) * int(x.q_lens[n])
+                                        - int(x.q_lens[n]) * (int(x.q_lens[n]) - 1) // 2))
+        rec["cpu_baseline"] = {"value": work / tc / 1e12, "unit": "TFLOP/s",
+                               "cores": blas_threads(), "kind": "oracle",
+                               "sample": f"{done} sequences of this workload, one oracle call "
+                                         f"each ({tc:.1f} s)"}
+    return rec
 
 
-def bench_decode_fp8(tea, workloads, dev, stream, flush):
-    """attn_decode_paged_fp8 on decode_fp8_7 (stream + combine kernels)."""
+def bench_decode_fp8(tea, workloads, dev, stream, flush, cpu_budget_s=None):
+    """attn_decode_paged_fp8 on decode_fp8_7 (stream + combine kernels), and the
+    oracle on sampled sequences."""
     import torch
     x = workloads.decode_fp8_7()
     xq, kc, vc = x.q.to(dev), x.k_codes.to(dev), x.v_codes.to(dev)
@@ -219,12 +268,36 @@ def bench_decode_fp8(tea, workloads, dev, stream, flush):
     pages = int(((x.seq_lens.astype("int64") + x.page - 1) // x.page).sum())
     nbytes = tokens * x.Hkv * x.d * 2 + 2 * x.N * x.Hq * x.d * 2 + x.N * x.Hq * 4 + x.N * 4 + pages * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, E4M3 K/V pages, lengths "
-                      f"U[512,8192] (sum {tokens})", "kernel": "decode_stream_kernel<fp8>+"
-                      "decode_combine_kernel", "ms": ms, "value": gbs, "unit": "GB/s",
-            "algorithmic_bytes": nbytes, "bound": "hbm", "peak": PEAK_HBM_GBS,
-            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": n,
-            "tokens_per_s": tokens / (ms * 1e-3)}
+    rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, E4M3 K/V pages, lengths "
+                     f"U[512,8192] (sum {tokens})", "kernel": "decode_stream_kernel<fp8>+"
+                     "decode_combine_kernel", "ms": ms, "value": gbs, "unit": "GB/s",
+           "algorithmic_bytes": nbytes, "bound": "hbm", "peak": PEAK_HBM_GBS,
+           "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": n,
+           "tokens_per_s": tokens / (ms * 1e-3), "cpu_baseline": None}
+    del xq, kc, vc, bt, sl, xo, xl, ws
+    if cpu_budget_s:
+        import numpy as np
+
+        import oracle
+        qd = x.q.double().numpy()
+        kcodes, vcodes = x.k_codes.numpy(), x.v_codes.numpy()
+
+        def one_sequence(n):
+            # the pages sequence n uses, as a pool of their own with the table renumbered
+            nb = (int(x.seq_lens[n]) + x.page - 1) // x.page
+            pages = x.block_table[n, :nb]
+            oracle.decode_paged_fp8(qd[n:n + 1], kcodes[pages], vcodes[pages], x.k_scale,
+                                    x.v_scale, np.arange(nb, dtype=np.int32)[None, :],
+                                    x.seq_lens[n:n + 1], x.scale, page=x.page)
+
+        done, work, tc = oracle_sample(
+            cpu_budget_s, list(range(x.N)), one_sequence,
+            lambda n: int(x.seq_lens[n]) * x.Hkv * x.d * 2 + 2 * x.Hq * x.d * 2)
+        rec["cpu_baseline"] = {"value": work / tc / 1e9, "unit": "GB/s", "cores": blas_threads(),
+                               "kind": "oracle",
+                               "sample": f"{done} sequences of this workload, one oracle call "
+                                         f"each on the E4M3 pages it uses ({tc:.1f} s)"}
+    return rec
 
 
 def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
@@ -505,9 +578,10 @@ def main():
             del xq, xk, xv, xo, xl
         out["prefill_other"] = other
     if not args.no_next:
-        out["window"] = bench_window(tea, workloads, dev, stream, flush)
-        out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush)
-        out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush)
+        nb = None if args.no_cpu_baseline else args.cpu_budget / 5
+        out["window"] = bench_window(tea, workloads, dev, stream, flush, nb)
+        out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush, nb)
+        out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush, nb)
     if not args.no_backward:
         out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
                                          None if args.no_cpu_baseline else args.cpu_budget / 3)
