@@ -91,6 +91,12 @@ def prefill_work(B, Hq, Hkv, T, S, d, causal, elem, window=0):
     return flops, nbytes
 
 
+def chunked_pairs(seq_lens, q_lens):
+    """Visible (query, key) pairs of a chunked prefill: the chunk's row i of a
+    sequence with L cached tokens (its T new ones last) sees L - T + i + 1 keys."""
+    return sum(int(L) * int(T) - int(T) * (int(T) - 1) // 2 for L, T in zip(seq_lens, q_lens))
+
+
 def decode_work(inp):
     tokens = int(inp.seq_lens.astype("int64").sum())
     pages = int(((inp.seq_lens.astype("int64") + inp.page - 1) // inp.page).sum())
@@ -225,9 +231,7 @@ def bench_chunked(tea, workloads, dev, stream, flush, cpu_budget_s=None):
     xl = torch.empty((x.N, x.Hq, x.T), dtype=torch.float32, device=dev)
     ms, n = timed_launches(stream, flush, lambda: tea.attn_prefill_paged(
         xq, kp, vp, bt, sl, ql, xo, xl, x.scale, stream=stream))
-    pairs = sum(int(L) * int(T) - int(T) * (int(T) - 1) // 2
-                for L, T in zip(x.seq_lens, x.q_lens))   # row i sees L - T + i + 1 keys
-    fl = 4 * x.d * x.Hq * pairs
+    fl = 4 * x.d * x.Hq * chunked_pairs(x.seq_lens, x.q_lens)
     tf = fl / (ms * 1e-3) / 1e12
     rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, chunk {x.T}, cached "
                      f"{int(x.seq_lens.min())}..{int(x.seq_lens.max())} tokens, d={x.d}, bf16, "
