@@ -1,4 +1,4 @@
-"""GPU parity where element offsets pass 2^31 (needs an MI355X; ~20 GB of HBM).
+"""GPU parity where element offsets pass 2^31 (needs an MI355X; up to ~50 GB of HBM).
 
 The kernels address one head (or one page) with 32-bit offsets from a 64-bit
 base; these cases make the bases themselves exceed 2^31 elements, so a base
@@ -6,8 +6,9 @@ computed in 32 bits would wrap to the wrong head or page.  The inputs are
 drawn on the device from a seeded torch generator (host generation of ~7.5e9
 values would take minutes); only the checked heads and sequences come back to
 the host, where the float64 oracle recomputes them.  Checked: the first head,
-heads whose offsets lie past 2^31, and the very last head; for decode,
-sequences whose pages sit at the top of a pool of more than 2^31 elements.
+heads whose offsets lie past 2^31, and the very last head (prefill and the
+backward pass); for decode and chunked prefill, sequences whose pages sit at
+the top of a pool of more than 2^31 elements.
 """
 import numpy as np
 import pytest
@@ -129,5 +130,68 @@ def test_decode_pages_past_2_31_elements(fp8):
         name = f"sequence {n} (top page {int(table[n, :nb].max())})"
         check_o(to_np(o[n:n + 1]), o_ref, "bf16", name)
         check_lse(to_np(lse[n:n + 1]), lse_ref, name)
+    del q, kp, vp, o, lse
+    torch.cuda.empty_cache()
+
+
+def test_backward_heads_past_2_31_elements():
+    """q, k, v, o, dO and the three gradients of 2.5e9 elements each (~50 GB)."""
+    from tests.gpu_helpers import check_grad
+    B, H, T, d = 2048, 32, 300, 128
+    assert B * H * T * d > TWO31
+    announce(f"attn_bwd large offsets: B={B} Hq=Hkv={H} T=S={T} d={d} causal")
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    q, k, v, do = (_randn((B, H, T, d), gen) for _ in range(4))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = tea.fwd(q, k, v, scale=scale, causal=True)
+    dq, dk, dv = tea.bwd(q, k, v, o, lse, do, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    first_past = TWO31 // (T * d) + 1
+    for bh in (0, first_past, B * H - 1):
+        b, h = divmod(bh, H)
+        host = [x[b, h].double().cpu().numpy() for x in (q, k, v, do)]
+        rq, rk, rv, _, _ = oracle.attention_head_backward(*host, scale, True)
+        for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
+            check_grad(to_np(got[b, h]), ref, f"head b={b} h={h} {what}")
+    del q, k, v, do, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
+
+
+def test_chunked_prefill_pages_past_2_31_elements():
+    """Chunks of 4 sequences against a pool of 1.15 * 2^31 elements, half of
+    each block table in its top pages."""
+    N, Hq, Hkv, d, page, T = 4, 12, 2, 128, 16, 256
+    per_page = Hkv * page * d
+    num_pages = TWO31 // per_page + 80_000
+    rng = np.random.default_rng(91)
+    lens = rng.integers(2000, 6001, N).astype(np.int32)
+    q_lens = np.array([T, T - 1, 100, 1], dtype=np.int32)
+    table = _decode_tables(num_pages, lens, rng, page)
+    assert int(table.max()) * per_page > TWO31
+    announce(f"attn_prefill_paged large offsets: {num_pages} pages, lens {lens.tolist()}, "
+             f"chunks {q_lens.tolist()}")
+    gen = torch.Generator(device="cuda").manual_seed(13)
+    q = _randn((N, Hq, T, d), gen)
+    kp = _randn((num_pages, Hkv, page, d), gen)
+    vp = _randn((num_pages, Hkv, page, d), gen)
+    o = torch.zeros_like(q)
+    lse = torch.zeros((N, Hq, T), dtype=torch.float32, device="cuda")
+    scale = 1.0 / np.sqrt(d)
+    tea.attn_prefill_paged(q, kp, vp, torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(),
+                           torch.from_numpy(q_lens).cuda(), o, lse, scale)
+    torch.cuda.synchronize()
+    qd = q.double().cpu().numpy()
+    for n in range(N):
+        nb = (int(lens[n]) + page - 1) // page
+        pages = torch.from_numpy(table[n, :nb].astype(np.int64)).cuda()
+        sub_k = kp.index_select(0, pages).cpu().double().numpy()
+        sub_v = vp.index_select(0, pages).cpu().double().numpy()
+        o_ref, lse_ref = oracle.prefill_paged(qd[n:n + 1], sub_k, sub_v,
+                                              np.arange(nb, dtype=np.int32)[None, :],
+                                              lens[n:n + 1], q_lens[n:n + 1], scale, page=page)
+        t = int(q_lens[n])
+        name = f"sequence {n} ({t} new of {int(lens[n])}, top page {int(table[n, :nb].max())})"
+        check_o(to_np(o[n, :, :t]), o_ref[0, :, :t], "bf16", name)
+        check_lse(to_np(lse[n, :, :t]), lse_ref[0, :, :t], name)
     del q, kp, vp, o, lse
     torch.cuda.empty_cache()
