@@ -380,10 +380,11 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           }
     }
 
-    // online softmax update (base 2), per row block
+    // online softmax update (base 2)
+    // row maximum of the tile per lane: a three-input max tree over its 4 NKB scores
+    float mloc[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      // row maximum of the tile: a three-input max tree over its 4 NKB scores
       float mk[4 * NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -400,28 +401,42 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
             mk[i] = max3_raw(a, b, c);
           }
         }
-      // The reference maximum only moves when the tile's maximum exceeds it
-      // by more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau
-      // and the accumulator is rarely rescaled; any reference gives the same
-      // O and LSE (it cancels between acc and l), only the rounding changes.
-      // A row's maximum can only pass that bar if one of its four lanes' own
-      // maxima does (scale > 0), so the cross-lane maximum, the new
-      // reference and the rescale factor are only formed on tiles where some
-      // lane of the wave passes it; elsewhere nothing moves and alpha is 1.
-      float alpha = 1.f;
-      if (wave_any(mk[0] * scale_log2 > m_run[qb] + kLazyTau)) {   // always when m_run = -inf
-        const float m_tile = pair_max32_raw(pair_max16_raw(mk[0])) * scale_log2;
+      mloc[qb] = mk[0];
+    }
+    // The reference maximum only moves when the tile's maximum exceeds it by
+    // more than kLazyTau (log2 units), so exponents stay <= 2^kLazyTau and
+    // the accumulator is rarely rescaled; any reference gives the same O and
+    // LSE (it cancels between acc and l), only the rounding changes.  A row's
+    // maximum can only pass that bar if one of its four lanes' own maxima does
+    // (scale > 0), so the cross-lane maxima, the new references and the
+    // rescale factors are only formed on tiles where some lane of the wave
+    // passes it for some row block (one vote and one branch per tile);
+    // elsewhere nothing moves and alpha is 1.
+    float alpha[QB];
+    bool pass = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      alpha[qb] = 1.f;
+      pass |= mloc[qb] * scale_log2 > m_run[qb] + kLazyTau;   // always when m_run = -inf
+    }
+    if (wave_any(pass)) {
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float m_tile = pair_max32_raw(pair_max16_raw(mloc[qb])) * scale_log2;
         const bool grow = m_tile > m_run[qb] + kLazyTau;
         const float m_new = grow ? m_tile : m_run[qb];
         const float m_off = (m_new == -INFINITY) ? 0.f : m_new;
-        alpha = exp2_hw(m_run[qb] - m_off);
+        alpha[qb] = exp2_hw(m_run[qb] - m_off);
         m_run[qb] = m_new;
         m_use[qb] = m_off;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha;
+          for (int i = 0; i < 4; ++i) acc[qb][db][i] *= alpha[qb];
       }
+    }
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
       float rs = 0.f;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
@@ -431,7 +446,7 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           s[qb][kb][i] = p;
           rs += p;
         }
-      l_part[qb] = __builtin_fmaf(l_part[qb], alpha, rs);
+      l_part[qb] = __builtin_fmaf(l_part[qb], alpha[qb], rs);
     }
 
     // O^T += V^T P^T, 32 keys at a time; each V operand feeds both row blocks
