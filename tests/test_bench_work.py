@@ -55,3 +55,15 @@ def test_decode_bytes_and_flops_by_explicit_sum():
     assert tokens == sum(L)
     assert nbytes == kv + table + qo + inp.N * inp.Hq * 4 + inp.N * 4
     assert flops == sum(4 * inp.d * l * inp.Hq for l in L)
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU's share; asked for more it says so and exits non-zero."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "one GPU" in (r.stdout + r.stderr)
