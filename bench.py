@@ -1,52 +1,59 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass of the whole path on resident synthetic inputs:
-  1. causal prefill attn_fwd on the GPT-2-small-shaped workload
-     (B=8, H=12, T=S=1024, d=64, bf16; override with --prefill), then
-  2. paged decode attn_decode_paged on 64 sequences, 12 query / 2 KV heads,
-     d=128, 16-token pages, lengths U[512, 8192] (stream kernel + combine).
+One step = one pass of the whole path on resident synthetic inputs, each
+launch preceded by a 512 MiB read that evicts L2 and the Infinity Cache:
+  1. causal prefill attn_fwd on the three prefill workloads:
+     prefill_2 (GPT-2-small-shaped: B=8, H=12, T=S=1024, d=64, bf16),
+     prefill_3 (GQA: B=4, Hq=12, Hkv=2, T=S=4096, d=128, bf16),
+     prefill_4 (long: B=1, H=32, T=S=16384, d=128, bf16, inputs x0.5);
+  2. paged decode attn_decode_paged on decode_5: 64 sequences, 12 query / 2 KV
+     heads, d=128, 16-token pages, lengths U[512, 8192] (stream kernel +
+     combine).
+`--only <workload>` makes the step that one launch (profiling runs).
 
 Reported (one JSON line on stdout):
-  value          causal-prefill TFLOP/s = algorithmic FLOPs / mean kernel time
-                 (HIP events on the launch stream), FLOPs = 4*d per visible
-                 (query, key) pair;
-  decode         paged-decode GB/s = algorithmic bytes / mean time of the stream
-                 + combine kernels, bytes = K+V of every cached token once plus
-                 q, o, lse, seq_lens and the used block-table entries;
-  roofline       the kernel that takes the most time per step against its
-                 published peak (bf16 dense MFMA 2516.6 TFLOP/s, HBM 8 TB/s);
-                 `traffic` comes from profiles/counters.json when the measured
-                 kernel sources still match the recorded hash, else null;
-  prefill_other  the same causal prefill timing on the two larger prefill
-                 workloads (GQA B=4 T=4096 d=128; long B=1 H=32 T=16384 d=128);
-  window         attn_fwd_window on the GQA causal workload with a 1024-key
-                 sliding window (FLOPs over the visible pairs only);
-  chunked        attn_prefill_paged on 16 sequences of 1024..8192 cached
-                 tokens whose last 512 are the new chunk, Hq=12, Hkv=2,
-                 d=128, keys through the block table (FLOPs over the
-                 visible pairs);
-  decode_fp8     attn_decode_paged_fp8 on decode_5's shape with E4M3 pages
-                 (decode_fp8_7): GB/s over the bytes it must read (one byte
-                 per cached K/V element, plus q, o, lse, lengths, block table);
-  (window, chunked and decode_fp8 each carry their own cpu_baseline: the
-  oracle timed on sampled heads or sequences of the same workload)
-  backward       the gradient pass attn_bwd (D = rowsum(dO*O), dQ, dK/dV
-                 kernels) on the GQA causal workload (B=4, Hq=12, Hkv=2,
-                 T=S=4096, d=128), TFLOP/s with FLOPs = 10*d per visible
-                 (query, key) pair (recomputed scores, dP, dV, dQ, dK: five
-                 products of 2*d each), next to the float64 backward oracle
-                 timed on a bounded sample of its heads;
-  cpu_baseline   the float64 oracle timed on the host on a bounded sample of
-                 the same workloads.
-`--write-counters DIR` turns rocprofv3 FETCH_SIZE / WRITE_SIZE collections
-(DIR/{bench,copy}_{fetch,write}/*_counter_collection.csv, taken on this script
-with the default workload and with --copy-probe) into profiles/counters.json:
-HBM bytes per launch, each counter scaled by what it reads for a copy of
-known size.
-Between steps a 512 MiB buffer is read (summed) so both kernels start with
-cold L2 / Infinity Cache without dirty lines whose write-back would compete
-with them; that read is outside the kernel events but inside ms_per_step.
+  value               prefill_2 TFLOP/s = algorithmic FLOPs / mean launch time
+                      (HIP events on the launch stream), FLOPs = 4*d per visible
+                      (query, key) pair;
+  roofline_per_kernel every workload of the step against its published peak
+                      (bf16 dense MFMA 2516.6 TFLOP/s; HBM 8 TB/s for decode,
+                      bytes = K+V of every cached token once plus q, o, lse,
+                      seq_lens and the used block-table entries), with its
+                      measured HBM traffic per launch (`traffic`, from
+                      profiles/counters.json while the kernel sources still
+                      match the recorded hash, else null) and the float64
+                      oracle timed on a bounded sample of the same workload on
+                      the host cores (`cpu_baseline`);
+  roofline            the entry of the workload that takes the most time;
+  hbm_probe           a read-only kernel (libattn_probe.so) on the decode
+                      workload's key/value chunks in the decode's order and grid
+                      shape, and on as many bytes in sequence: the read rate
+                      the chip reaches on those bytes with no compute;
+  window              attn_fwd_window on prefill_3's inputs with a 1024-key
+                      sliding window (FLOPs over the visible pairs only);
+  chunked             attn_prefill_paged on 16 sequences of 1024..8192 cached
+                      tokens whose last 512 are the new chunk, Hq=12, Hkv=2,
+                      d=128, keys through the block table;
+  decode_fp8          attn_decode_paged_fp8 on decode_5's shape with E4M3 pages
+                      (decode_fp8_7): GB/s over the bytes it must read;
+  backward            the gradient pass attn_bwd on prefill_3's shape,
+                      TFLOP/s with FLOPs = 10*d per visible (query, key) pair
+                      (recomputed scores, dP, dV, dQ, dK);
+  (window, chunked, decode_fp8 and backward each carry their own cpu_baseline)
+  cpu_baseline        the oracle's figure for the headline workload.
+The flush reads sit outside the kernel events but inside ms_per_step.
+
+Measurement helpers (each runs and exits):
+  --copy-probe        a 256 MiB device copy, to calibrate the HBM counters;
+  --hbm-probe         the read-only probe alone;
+  --write-counters D  profiles/counters.json from rocprofv3 FETCH_SIZE /
+                      WRITE_SIZE collections under D (D/copy_{fetch,write}
+                      from --copy-probe runs, D/<workload>_{fetch,write} from
+                      --only <workload> runs): HBM bytes per launch, each
+                      counter scaled by what it reads for a copy of known size;
+  --summarize D       a markdown table of a rocprofv3 kernel trace or counter
+                      collection under D, per kernel and grid size.
 """
 import argparse
 import hashlib
@@ -126,47 +133,6 @@ def oracle_sample(budget_s, units, run_unit, work_of):
         work += work_of(u)
         done += 1
     return done, work, time.perf_counter() - t0
-
-
-def cpu_baseline(pinp, dinp, budget_s):
-    """Time the oracle on a bounded sample of both workloads (host cores).
-
-    Whole passes over the (batch, head) pairs of the prefill workload, then
-    over the sequences of the decode workload, are repeated until about 70 %
-    (prefill) and 30 % (decode) of budget_s is spent; a pass that runs out of
-    budget stops where it is, so the sample is a prefix of the workload
-    repeated."""
-    import numpy as np
-
-    import oracle
-    q, k, v = (t.double().numpy() for t in (pinp.q, pinp.k, pinp.v))
-    g = pinp.Hq // pinp.Hkv
-    heads = [(b, h) for b in range(pinp.B) for h in range(pinp.Hq)]
-    head_flops = prefill_work(1, 1, 1, pinp.T, pinp.S, pinp.d, pinp.causal, 2)[0]
-    done, t0 = 0, time.perf_counter()
-    while time.perf_counter() - t0 < budget_s * 0.7:
-        b, h = heads[done % len(heads)]
-        oracle.attention_head(q[b, h], k[b, h // g], v[b, h // g], pinp.scale, pinp.causal)
-        done += 1
-    tp = time.perf_counter() - t0
-    qd, kd, vd = dinp.f64()
-    nseq, dbytes, t1 = 0, 0, time.perf_counter()
-    while time.perf_counter() - t1 < budget_s * 0.3:
-        n = nseq % dinp.N
-        oracle.decode_paged(qd, kd, vd, dinp.block_table, dinp.seq_lens, dinp.scale, seqs=[n])
-        L = int(dinp.seq_lens[n])
-        dbytes += L * dinp.Hkv * dinp.d * 4 + 2 * dinp.Hq * dinp.d * 2
-        nseq += 1
-    td = time.perf_counter() - t1
-    return {
-        "value": done * head_flops / tp / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
-        "kind": "oracle",
-        "sample": f"{done} (batch, head) attention problems of {pinp.name} ({done / len(heads):.2f} "
-                  f"passes over its {len(heads)}, {tp:.1f} s); decode: {nseq} sequences of "
-                  f"{dinp.name} ({nseq / dinp.N:.2f} passes over its {dinp.N}, {td:.1f} s)",
-        "decode_value": dbytes / td / 1e9, "decode_unit": "GB/s",
-        "host_cpus": len(os.sched_getaffinity(0)),
-    }
 
 
 def timed_launches(stream, flush, launch, n=7, skip=2):
@@ -353,59 +319,179 @@ def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
     return rec
 
 
+# --- the main step: causal prefill on the three prefill workloads, then decode ----
+
+MAIN_STEP = ["prefill_2", "prefill_3", "prefill_4", "decode_5"]
+HEADLINE = "prefill_2"
+# Kernel names (substrings) per workload, for traces and counters.
+KERNEL_OF = {"prefill_2": "prefill_bf16_kernel", "prefill_3": "prefill_bf16_kernel",
+             "prefill_4": "prefill_bf16_kernel",
+             "decode_5": "decode_stream_kernel+decode_combine_kernel"}
+# Oracle seconds per workload out of --cpu-budget (fractions).
+CPU_SHARE = {"prefill_2": 0.3, "prefill_3": 0.25, "prefill_4": 0.25, "decode_5": 0.2}
+
+
+def prefill_grid_threads(x):
+    """Threads of one prefill launch (the grid the kernel trace reports): 128 query
+    rows per 256-thread workgroup, or 64 rows per workgroup on grids under 256
+    workgroups."""
+    wgs = -(-x.T // 128) * x.B * x.Hq
+    if wgs < 256:
+        wgs = -(-x.T // 64) * x.B * x.Hq
+    return wgs * 256
+
+
+def oracle_prefill_sample(x, budget_s, window=0):
+    """Float64 oracle on (batch, head) problems of prefill workload x, in order
+    and cycling, for about budget_s seconds."""
+    import oracle
+    g = x.Hq // x.Hkv
+    heads = [(b, h) for b in range(x.B) for h in range(x.Hq)]
+    fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2, window=window)
+    q, k, v = x.q, x.k, x.v
+    done, work, tc = oracle_sample(
+        budget_s, heads,
+        lambda bh: oracle.attention_head(q[bh[0], bh[1]].double().numpy(),
+                                         k[bh[0], bh[1] // g].double().numpy(),
+                                         v[bh[0], bh[1] // g].double().numpy(),
+                                         x.scale, x.causal, window=window),
+        lambda bh: fl // len(heads))
+    return {"value": work / tc / 1e12, "unit": "TFLOP/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"{done} (batch, head) attention problems of {x.name} ({done / len(heads):.2f} "
+                      f"passes over its {len(heads)}, {tc:.1f} s, {fl // len(heads) * done / 1e9:.1f} "
+                      f"GFLOP)", "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def oracle_decode_sample(x, budget_s):
+    """Float64 oracle on whole sequences of decode workload x for about budget_s
+    seconds; GB/s over the same algorithmic bytes per sequence as the GPU figure."""
+    import oracle
+    qd, kd, vd = x.f64()
+
+    def one(n):
+        oracle.decode_paged(qd, kd, vd, x.block_table, x.seq_lens, x.scale, seqs=[n])
+
+    def nbytes(n):
+        L = int(x.seq_lens[n])
+        return L * x.Hkv * x.d * 2 * 2 + 2 * x.Hq * x.d * 2 + x.Hq * 4 + 4 + -(-L // x.page) * 4
+
+    done, work, tc = oracle_sample(budget_s, list(range(x.N)), one, nbytes)
+    return {"value": work / tc / 1e9, "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{done} sequences of {x.name} ({done / x.N:.2f} passes over its {x.N}, "
+                      f"{tc:.1f} s), one oracle call each", "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def hbm_probe(dinp, dev, stream, flush, launches=12):
+    """Read-only probe (libattn_probe.so): the decode workload's key and value
+    slabs, one 4 KiB chunk each per (page, KV head), read in the decode's
+    sequence-major order by the decode's grid shape; then the same byte count
+    read in order from a contiguous buffer.  GB/s = bytes / mean event time."""
+    import ctypes
+
+    import numpy as np
+    import torch
+    from tiled_exact_attention_flashattention_amd import build as B
+    if not os.path.exists(B.PROBE_LIB_PATH):
+        raise RuntimeError(f"{B.PROBE_LIB_PATH} is missing: build with "
+                           "`python -m tiled_exact_attention_flashattention_amd.build`")
+    L = ctypes.CDLL(B.PROBE_LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int
+    L.attn_probe_read_units.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp]
+    L.attn_probe_read_units.restype = i32
+    unit_bytes = dinp.page * dinp.d * 2
+    units = []
+    for n in range(dinp.N):
+        nb = -(-int(dinp.seq_lens[n]) // dinp.page)
+        for hk in range(dinp.Hkv):
+            units.append(dinp.block_table[n, :nb].astype(np.int64) * dinp.Hkv + hk)
+    units = np.concatenate(units).astype(np.int32)
+    pool_units = dinp.k_pool.numel() * 2 // unit_bytes
+    assert units.min() >= 0 and units.max() < pool_units
+    waves = 1024
+    sink = torch.empty(waves * 64, dtype=torch.int32, device=dev)
+    kp, vpl = dinp.k_pool.to(dev), dinp.v_pool.to(dev)
+    u_dev = torch.from_numpy(units).to(dev)
+    n = len(units)
+    seq = torch.empty(2 * n * unit_bytes, dtype=torch.uint8, device=dev)
+    seq_units = torch.arange(n, dtype=torch.int32, device=dev)
+    res = {}
+    for name, (kb, vb, ub) in {"decode_pages": (kp, vpl, u_dev),
+                               "sequential": (seq, seq[n * unit_bytes:], seq_units)}.items():
+        def launch():
+            st = L.attn_probe_read_units(kb.data_ptr(), vb.data_ptr(), ub.data_ptr(), n, unit_bytes,
+                                         sink.data_ptr(), waves, ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"probe launch failed ({st})")
+        ms, cnt = timed_launches(stream, flush, launch, n=launches, skip=2)
+        nbytes = 2 * n * unit_bytes
+        res[name] = {"bytes": nbytes, "ms": ms, "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+                     "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                     "launches": cnt}
+    res["note"] = (f"{n} chunks of {unit_bytes} B of K and as many of V ({waves} one-wave "
+                   "workgroups, equal contiguous ranges); cold caches")
+    del kp, vpl, u_dev, seq, seq_units, sink
+    return res
+
+
 def write_counters(pmc_dir):
-    """profiles/counters.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs."""
+    """profiles/counters.json from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE CSVs.
+
+    Expects DIR/copy_{fetch,write}/ (this script with --copy-probe) and
+    DIR/<workload>_{fetch,write}/ for each workload of the main step (this
+    script with --only <workload>); every dispatch of the workload's kernels is
+    averaged, the flush's reduction kernel excluded by name."""
     import csv
     import glob
 
-    def per_kernel(sub):
-        files = glob.glob(os.path.join(pmc_dir, sub, "*_counter_collection.csv"))
+    def rows(sub):
+        files = glob.glob(os.path.join(pmc_dir, sub, "**", "*_counter_collection.csv"), recursive=True)
         if len(files) != 1:
             raise SystemExit(f"need exactly one counter_collection.csv under {pmc_dir}/{sub}")
-        vals = {}
-        for r in csv.DictReader(open(files[0])):
-            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return vals
+        return list(csv.DictReader(open(files[0])))
 
     copy_bytes = 256 << 20
     factors = {}
     for counter, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
-        vals = per_kernel(sub)
         # the copy is the dispatch with the largest reading (KiB per dispatch)
-        kib = max(max(v) for v in vals.values())
+        kib = max(float(r["Counter_Value"]) for r in rows(sub))
         factors[counter] = copy_bytes / (kib * 1024.0)
-    fetch, write = per_kernel("bench_fetch"), per_kernel("bench_write")
-
-    def bytes_of(pattern):
-        tot = {}
-        for counter, vals in (("FETCH_SIZE", fetch), ("WRITE_SIZE", write)):
-            kib = sum(sum(v) / len(v) for k, v in vals.items() if any(p in k for p in pattern))
-            tot[counter] = kib * 1024.0 * factors[counter]
-        return tot
 
     out = {"factors": factors, "copy_probe_bytes": copy_bytes,
            "commands": {"copy": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
                                 "-- python3 bench.py --copy-probe",
-                        "bench": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
-                                 "-- python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-flush --no-other-prefill "
-                                 "--no-backward --no-next"}}
-    for kind, pattern in (("prefill", ["prefill_bf16_kernel"]),
-                          ("decode", ["decode_stream_kernel", "decode_combine_kernel"])):
-        t = bytes_of(pattern)
-        out[kind] = {"sources_sha": sources_sha(kind), "kernels": pattern,
-                     "fetch_bytes_per_launch": t["FETCH_SIZE"], "write_bytes_per_launch": t["WRITE_SIZE"],
-                     "hbm_bytes_per_launch": t["FETCH_SIZE"] + t["WRITE_SIZE"]}
+                        "workload": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
+                                    "-- python3 bench.py --only <workload> --steps 3 --warmup 1 "
+                                    "--no-cpu-baseline (flush on: cold caches as in the timed run)"}}
+    for name in MAIN_STEP:
+        kinds = KERNEL_OF[name].split("+")
+        kind = "decode" if name.startswith("decode") else "prefill"
+        tot = {}
+        for counter, suffix in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            per = {}
+            for r in rows(f"{name}_{suffix}"):
+                if any(k in r["Kernel_Name"] for k in kinds):
+                    per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            if not per:
+                raise SystemExit(f"no {kinds} dispatch in {name}_{suffix}")
+            kib = sum(sum(v) / len(v) for v in per.values())
+            tot[counter] = kib * 1024.0 * factors[counter]
+        out[name] = {"sources_sha": sources_sha(kind), "kernels": kinds,
+                     "fetch_bytes_per_launch": tot["FETCH_SIZE"],
+                     "write_bytes_per_launch": tot["WRITE_SIZE"],
+                     "hbm_bytes_per_launch": tot["FETCH_SIZE"] + tot["WRITE_SIZE"]}
     path = os.path.join(ROOT, "profiles", "counters.json")
     with open(path, "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
 
-def counters_for(kind):
+def counters_for(name):
     path = os.path.join(ROOT, "profiles", "counters.json")
+    kind = "decode" if name.startswith("decode") else "prefill"
     try:
         with open(path) as f:
-            rec = json.load(f).get(kind)
+            rec = json.load(f).get(name)
     except (OSError, ValueError):
         return None
     if not rec or rec.get("sources_sha") != sources_sha(kind):
@@ -413,28 +499,79 @@ def counters_for(kind):
     return rec.get("hbm_bytes_per_launch")
 
 
+def summarize(prof_dir):
+    """Markdown summary of a rocprofv3 run under prof_dir: per (kernel, grid)
+    dispatch count and mean / min / max duration from the kernel trace, or the
+    mean of every counter per (kernel, grid) from a counter collection."""
+    import csv
+    import glob
+    from collections import defaultdict
+    traces = glob.glob(os.path.join(prof_dir, "**", "*_kernel_trace.csv"), recursive=True)
+    counters = glob.glob(os.path.join(prof_dir, "**", "*_counter_collection.csv"), recursive=True)
+    lines = []
+
+    def short(name):
+        return name.split("(")[0][:110]
+
+    for f in traces:
+        acc = defaultdict(list)
+        for r in csv.DictReader(open(f)):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            acc[(r["Kernel_Name"], grid)].append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        lines += [f"kernel trace `{os.path.relpath(f, prof_dir)}`", "",
+                  "| kernel | grid (threads) | dispatches | mean µs | min µs | max µs |",
+                  "|---|---|---|---|---|---|"]
+        for (k, g), d in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
+            lines.append(f"| `{short(k)}` | {g} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
+                         f"{max(d):.2f} |")
+        lines.append("")
+    for f in counters:
+        acc = defaultdict(lambda: defaultdict(list))
+        for r in csv.DictReader(open(f)):
+            acc[(r["Kernel_Name"], int(r["Grid_Size"]))][r["Counter_Name"]].append(
+                float(r["Counter_Value"]))
+        names = sorted({c for v in acc.values() for c in v})
+        lines += [f"counters `{os.path.relpath(f, prof_dir)}` (mean per dispatch)", "",
+                  "| kernel | grid | dispatches | " + " | ".join(names) + " |",
+                  "|---|---|---|" + "---|" * len(names)]
+        for (k, g), cs in sorted(acc.items(), key=lambda kv: kv[0][1]):
+            n = max(len(v) for v in cs.values())
+            vals = [f"{sum(cs[c]) / len(cs[c]):.4g}" if cs.get(c) else "" for c in names]
+            lines.append(f"| `{short(k)}` | {g} | {n} | " + " | ".join(vals) + " |")
+        lines.append("")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--prefill", default="prefill_2",
-                    choices=["prefill_2", "prefill_3", "prefill_4"])
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", choices=MAIN_STEP,
+                    help="the step runs only this workload (for profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
+                    help="seconds of oracle work for the main step's workloads")
     ap.add_argument("--no-flush", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 256 MiB device copy (counter calibration) and exit")
+    ap.add_argument("--hbm-probe", action="store_true",
+                    help="only run the read-only HBM probe on the decode workload's pages and exit")
     ap.add_argument("--write-counters", metavar="DIR",
                     help="write profiles/counters.json from rocprofv3 CSVs under DIR and exit")
-    ap.add_argument("--no-other-prefill", action="store_true",
-                    help="skip the timing of the two larger prefill workloads")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 output directory and exit")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass timing")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the sliding-window, chunked-prefill and fp8-decode timings")
+    ap.add_argument("--no-probe", action="store_true", help="skip the read-only HBM probe")
     args = ap.parse_args()
     if args.write_counters:
         write_counters(args.write_counters)
+        return
+    if args.summarize:
+        summarize(args.summarize)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -450,6 +587,10 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    # float32 so that sum() only reads it (an int32 sum would first write an
+    # int64 copy, leaving dirty cache lines whose write-back slows the kernels)
+    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
 
     if args.copy_probe:
         src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
@@ -459,39 +600,45 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 256 << 20, "launches": 5}))
         return
+    if args.hbm_probe:
+        print(json.dumps(hbm_probe(workloads.decode_5(), dev, stream, flush)), flush=True)
+        return
 
-    pinp = getattr(workloads, args.prefill)()
-    dinp = workloads.decode_5()
-    q, k, v = (t.to(dev) for t in (pinp.q, pinp.k, pinp.v))
-    o = torch.empty_like(q)
-    lse = torch.empty((pinp.B, pinp.Hq, pinp.T), dtype=torch.float32, device=dev)
-    dq, dk, dv = dinp.q.to(dev), dinp.k_pool.to(dev), dinp.v_pool.to(dev)
-    bt = torch.from_numpy(dinp.block_table).to(dev)
-    sl = torch.from_numpy(dinp.seq_lens).to(dev)
-    do = torch.empty_like(dq)
-    dlse = torch.empty((dinp.N, dinp.Hq), dtype=torch.float32, device=dev)
-    ws = tea.decode_workspace(dinp.N, dinp.Hq, dinp.d, dinp.max_blocks, dev)
-    # float32 so that sum() only reads it (an int32 sum would first write an
-    # int64 copy, leaving dirty cache lines whose write-back slows the kernels)
-    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
+    names = [args.only] if args.only else MAIN_STEP
+    inputs, launchers = {}, {}
+    for name in names:
+        x = getattr(workloads, name)()
+        inputs[name] = x
+        if name.startswith("prefill"):
+            q, k, v = (t.to(dev) for t in (x.q, x.k, x.v))
+            o = torch.empty_like(q)
+            lse = torch.empty((x.B, x.Hq, x.T), dtype=torch.float32, device=dev)
+            launchers[name] = (lambda q=q, k=k, v=v, o=o, lse=lse, x=x:
+                               tea.attn_fwd(q, k, v, o, lse, x.scale, x.causal, stream=stream))
+        else:
+            dq, dk, dv = x.q.to(dev), x.k_pool.to(dev), x.v_pool.to(dev)
+            bt = torch.from_numpy(x.block_table).to(dev)
+            sl = torch.from_numpy(x.seq_lens).to(dev)
+            do = torch.empty_like(dq)
+            dlse = torch.empty((x.N, x.Hq), dtype=torch.float32, device=dev)
+            ws = tea.decode_workspace(x.N, x.Hq, x.d, x.max_blocks, dev)
+            launchers[name] = (lambda dq=dq, dk=dk, dv=dv, bt=bt, sl=sl, do=do, dlse=dlse, ws=ws, x=x:
+                               tea.attn_decode_paged(dq, dk, dv, bt, sl, do, dlse, x.scale, ws,
+                                                     stream=stream))
 
-    stream = torch.cuda.current_stream(dev)
-    events = []
+    events = {name: [] for name in names}
 
     def step(record):
-        if flush is not None:
-            flush.sum()
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
-        if record:
-            e[0].record(stream)
-        tea.attn_fwd(q, k, v, o, lse, pinp.scale, pinp.causal, stream=stream)
-        if record:
-            e[1].record(stream)
-            e[2].record(stream)
-        tea.attn_decode_paged(dq, dk, dv, bt, sl, do, dlse, dinp.scale, ws, stream=stream)
-        if record:
-            e[3].record(stream)
-            events.append(e)
+        for name in names:
+            if flush is not None:
+                flush.sum()
+            if record:
+                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+            launchers[name]()
+            if record:
+                b_.record(stream)
+                events[name].append((a, b_))
 
     for _ in range(args.warmup):
         step(False)
@@ -502,32 +649,47 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    prefill_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
-    decode_ms = sum(e[2].elapsed_time(e[3]) for e in events) / len(events)
 
-    elem = 2 if pinp.dtype == "bf16" else 4
-    pflops, pbytes = prefill_work(pinp.B, pinp.Hq, pinp.Hkv, pinp.T, pinp.S, pinp.d, pinp.causal, elem)
-    dflops, dbytes, tokens = decode_work(dinp)
-    p_tflops = pflops / (prefill_ms * 1e-3) / 1e12
-    d_gbs = dbytes / (decode_ms * 1e-3) / 1e9
-    peak_p = PEAK_BF16_TFLOPS if pinp.dtype == "bf16" else PEAK_F32_TFLOPS
+    kernels = {}
+    for name in names:
+        x = inputs[name]
+        times = [a.elapsed_time(b_) for a, b_ in events[name]]
+        ms = sum(times) / len(times)
+        if name.startswith("prefill"):
+            fl, nb = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
+            rate = fl / (ms * 1e-3) / 1e12
+            rec = {"kernel": KERNEL_OF[name], "bound": "mfma", "achieved": rate,
+                   "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": rate / PEAK_BF16_TFLOPS,
+                   "config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal"
+                             f"{', inputs x0.5' if name == 'prefill_4' else ''}",
+                   "grid_threads": prefill_grid_threads(x)}
+        else:
+            fl, nb, tokens = decode_work(x)
+            rate = nb / (ms * 1e-3) / 1e9
+            rec = {"kernel": KERNEL_OF[name], "bound": "hbm", "achieved": rate,
+                   "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": rate / PEAK_HBM_GBS,
+                   "config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, page {x.page}, lengths "
+                             f"U[512,8192] (sum {tokens}), bf16", "tokens": tokens,
+                   "tokens_per_s": tokens / (ms * 1e-3)}
+        rec.update({"traffic": counters_for(name), "algorithmic_flops": fl,
+                    "algorithmic_bytes": nb, "ms": ms, "ms_min": min(times),
+                    "launches": len(times)})
+        kernels[name] = rec
 
-    kernels = {
-        "prefill": {"kernel": "prefill_bf16_kernel", "bound": "mfma", "achieved": p_tflops,
-                    "peak": peak_p, "unit": "TFLOP/s", "frac": p_tflops / peak_p,
-                    "traffic": counters_for("prefill"), "algorithmic_bytes": pbytes,
-                    "algorithmic_flops": pflops, "ms": prefill_ms},
-        "decode": {"kernel": "decode_stream_kernel+decode_combine_kernel", "bound": "hbm",
-                   "achieved": d_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                   "frac": d_gbs / PEAK_HBM_GBS, "traffic": counters_for("decode"),
-                   "algorithmic_bytes": dbytes, "algorithmic_flops": dflops, "ms": decode_ms},
-    }
-    dominant = "prefill" if prefill_ms >= decode_ms else "decode"
+    if not args.no_probe and "decode_5" in names:
+        probe = hbm_probe(inputs["decode_5"], dev, stream, flush)
+        kernels["decode_5"]["frac_of_probe_ceiling"] = (
+            kernels["decode_5"]["achieved"] / probe["decode_pages"]["value"])
+    else:
+        probe = None
 
+    dominant = max(names, key=lambda n: kernels[n]["ms"])
+    head = HEADLINE if HEADLINE in names else names[0]
+    hx = inputs[head]
     out = {
         "metric": "causal prefill attention TFLOP/s + paged decode GB/s, % of MFMA/HBM peak",
-        "value": p_tflops,
-        "unit": "TFLOP/s",
+        "value": kernels[head]["achieved"],
+        "unit": kernels[head]["unit"],
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -535,64 +697,41 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": pinp.dtype,
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{pinp.name} causal prefill (B={pinp.B}, Hq={pinp.Hq}, Hkv={pinp.Hkv}, "
-                        f"T=S={pinp.T}, d={pinp.d}, {pinp.dtype}) + {dinp.name} paged decode "
-                        f"(N={dinp.N}, Hq={dinp.Hq}, Hkv={dinp.Hkv}, d={dinp.d}, page {dinp.page}, "
-                        f"lengths U[512,8192], sum {tokens})",
-            "global_batch": pinp.B,
-            "seq_len": pinp.T,
+            "workload": f"{head}: {kernels[head]['config']}; the step also runs "
+                        + ", ".join(f"{n} ({kernels[n]['config']})" for n in names if n != head),
+            "global_batch": getattr(hx, "B", getattr(hx, "N", None)),
+            "seq_len": getattr(hx, "T", None),
             "parallelism": "single GPU",
             "cold_cache": flush is not None,
+            "step": names,
         },
-        "decode": {"value": d_gbs, "unit": "GB/s", "frac_of_hbm_peak": d_gbs / PEAK_HBM_GBS,
-                   "ms": decode_ms, "tokens": tokens},
-        "prefill_frac_of_mfma_peak": p_tflops / peak_p,
-        "roofline": dict(kernels[dominant]),
+        "roofline": dict(kernels[dominant], workload=dominant),
         "roofline_per_kernel": kernels,
     }
-    if not args.no_other_prefill:
-        other = {}
-        for name in ("prefill_3", "prefill_4"):
-            if name == pinp.name:
-                continue
-            x = getattr(workloads, name)()
-            xq, xk, xv = (t.to(dev) for t in (x.q, x.k, x.v))
-            xo = torch.empty_like(xq)
-            xl = torch.empty((x.B, x.Hq, x.T), dtype=torch.float32, device=dev)
-            times = []
-            for i in range(7):
-                if flush is not None:
-                    flush.sum()
-                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                tea.attn_fwd(xq, xk, xv, xo, xl, x.scale, x.causal, stream=stream)
-                b_.record(stream)
-                if i >= 2:
-                    times.append((a, b_))
-            torch.cuda.synchronize()
-            ms = sum(a.elapsed_time(b_) for a, b_ in times) / len(times)
-            fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
-            tf = fl / (ms * 1e-3) / 1e12
-            other[name] = {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal",
-                           "ms": ms, "value": tf, "unit": "TFLOP/s", "frac_of_mfma_peak": tf / peak_p,
-                           "launches": len(times)}
-            del xq, xk, xv, xo, xl
-        out["prefill_other"] = other
-    if not args.no_next:
-        nb = None if args.no_cpu_baseline else args.cpu_budget / 5
-        out["window"] = bench_window(tea, workloads, dev, stream, flush, nb)
-        out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush, nb)
-        out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush, nb)
-    if not args.no_backward:
-        out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
-                                         None if args.no_cpu_baseline else args.cpu_budget / 3)
+    if probe is not None:
+        out["hbm_probe"] = probe
+    if not args.only:
+        if not args.no_next:
+            nb_ = None if args.no_cpu_baseline else args.cpu_budget / 5
+            out["window"] = bench_window(tea, workloads, dev, stream, flush, nb_)
+            out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush, nb_)
+            out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush, nb_)
+        if not args.no_backward:
+            out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
+                                             None if args.no_cpu_baseline else args.cpu_budget / 3)
+    out["cpu_baseline"] = None
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(pinp, dinp, args.cpu_budget)
-    else:
-        out["cpu_baseline"] = None
+        for name in names:
+            x = inputs[name]
+            budget = args.cpu_budget * CPU_SHARE[name]
+            cb = (oracle_prefill_sample(x, budget) if name.startswith("prefill")
+                  else oracle_decode_sample(x, budget))
+            kernels[name]["cpu_baseline"] = cb
+        out["cpu_baseline"] = kernels[head]["cpu_baseline"]
+        out["roofline"]["cpu_baseline"] = kernels[dominant]["cpu_baseline"]
     print(json.dumps(out), flush=True)
 
 

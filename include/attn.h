@@ -83,6 +83,10 @@ typedef enum {
  *   lse [B, Hq,  T]     float32      natural-log log-sum-exp of the scaled
  *                                    logits of each row (written); may be NULL
  *
+ * "Advanced Attention Mechanisms - II" (A. Das), section Tiling, step 2 and
+ * section "Softmax stabiliser"; the tile-by-tile computation follows its
+ * section "Incremental / online softmax", and the log-sum-exp is the row
+ * statistic its section "Flash Attention" keeps instead of the matrix:
  * O[b,h,i,:] = sum_j P[i,j] V[b,hk,j,:] with P = softmax_j(scale * q_i . k_j)
  * over the visible keys j, where hk = h / (Hq / Hkv) (consecutive query heads
  * share a KV head; Hq == Hkv is ordinary multi-head, Hkv == 1 multi-query).
@@ -226,6 +230,12 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
  *               entry are ignored.  Two calls that share a workspace must not overlap
  *               in time (same stream, or ordered).
  *
+ * "Fast attention kernels and operator fusion accelerate AI models", section
+ * on paged attention: keys and values live in fixed-size pages, and a block
+ * table maps each logical block of a sequence to its physical page, which the
+ * kernel translates for every position (16-token blocks in its serving
+ * example); the attention over the gathered keys is attn_fwd's definition with
+ * one query row.
  * Token t of sequence n sits in page block_table[n, t / page] at slot
  * t % page.  The query attends every cached token t < seq_lens[n] (no mask
  * beyond the length).  The page pairs (32 tokens) of all (sequence, KV head)

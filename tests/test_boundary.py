@@ -256,6 +256,13 @@ def _dec(**kw):
     (dict(q=P + 4), ATTN_EINVAL), (dict(bt=4 * P + 2), ATTN_EINVAL),
     (dict(ws=None), ATTN_EINVAL), (dict(ws_bytes=WS - 1), ATTN_EINVAL), (dict(ws=8 * P + 8), ATTN_EINVAL),
     (dict(N=4096, Hkv=12, Hq=12, max_blocks=1 << 17, ws_bytes=1 << 40), ATTN_EINVAL),   # > 2^31 pairs
+    (dict(o=P), ATTN_EINVAL),                    # output aliases q
+    (dict(o=5 * P), ATTN_EINVAL),                # output over seq_lens
+    (dict(lse=4 * P + 64), ATTN_EINVAL),         # lse inside the block table
+    (dict(lse=6 * P + 64), ATTN_EINVAL),         # lse inside o
+    (dict(ws=2 * P), ATTN_EINVAL),               # workspace over the key pool
+    (dict(ws=6 * P - 1024), ATTN_EINVAL),        # workspace runs into o
+    (dict(o=8 * P + 4096), ATTN_EINVAL),         # o inside the workspace
 ])
 def test_decode_rejects_bad_arguments(bad, code):
     assert _dec(**bad) == code
@@ -278,6 +285,8 @@ def _dec8(k_scale=0.03, v_scale=0.03, **kw):
     ((0.03, 0.03), dict(q=None), ATTN_EINVAL), ((0.03, 0.03), dict(page=8), ATTN_EUNSUPPORTED),
     ((0.03, 0.03), dict(d=96), ATTN_EUNSUPPORTED), ((0.03, 0.03), dict(ws_bytes=WS - 1), ATTN_EINVAL),
     ((0.03, 0.03), dict(k=2 * P + 8), ATTN_EINVAL), ((0.03, 0.03), dict(Hq=34, Hkv=2), ATTN_EUNSUPPORTED),
+    ((0.03, 0.03), dict(ws=3 * P), ATTN_EINVAL),             # workspace over the value pool
+    ((0.03, 0.03), dict(lse=P + 16), ATTN_EINVAL),           # lse inside q
 ])
 def test_decode_fp8_rejects_bad_arguments(scales, bad, code):
     assert _dec8(*scales, **bad) == code

@@ -303,6 +303,24 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
     return fail(ATTN_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
                 workspace_bytes);
   if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "%s: misaligned workspace", fn);
+  {
+    const size_t es = fp8 ? 1 : 2;
+    const size_t qb = (size_t)N * Hq * d * 2, pb = (size_t)num_pages * Hkv * kPage * d * es;
+    const size_t btb = (size_t)N * max_blocks * 4, nb = (size_t)N * 4;
+    const size_t lb = lse ? (size_t)N * Hq * 4 : 0;
+    const void* ins[] = {q, k_pool, v_pool, block_table, seq_lens};
+    const size_t in_bytes[] = {qb, pb, pb, btb, nb};
+    void* outs[] = {o, lse, workspace};
+    const size_t out_bytes[] = {qb, lb, lay.total};
+    for (int a = 0; a < 3; ++a) {
+      for (int i = 0; i < 5; ++i)
+        if (overlap(outs[a], out_bytes[a], ins[i], in_bytes[i]))
+          return fail(ATTN_EINVAL, "%s: o, lse or the workspace overlaps an input", fn);
+      for (int c = a + 1; c < 3; ++c)
+        if (overlap(outs[a], out_bytes[a], outs[c], out_bytes[c]))
+          return fail(ATTN_EINVAL, "%s: o, lse and the workspace must not overlap", fn);
+    }
+  }
 
   char* ws = static_cast<char*>(workspace);
   attn::DecodeWorkspace dw;

@@ -18,10 +18,11 @@
 //     operands, K and V tiles stream through two LDS stages by the
 //     direct-to-LDS load; per tile S^T = K Q^T, dP^T = V dO^T, P, dS, and
 //     dQ^T += K^T dS^T with K^T from the LDS transpose read.
-//   bwd_dkdv_kernel:  one workgroup per 64 keys of one (batch, KV head); each
-//     wave keeps its 16 keys' K and V in registers as MFMA B operands and
-//     walks every query tile (32 rows) of every query head of the group that
-//     can see them.  Q and dO tiles and their rows' statistics stream through
+//   bwd_dkdv_kernel:  one workgroup per 128 keys of one (batch, KV head), one
+//     wave per SIMD; each wave keeps its 32 keys' K and V (two 16-key blocks)
+//     in registers as MFMA B operands and walks every query tile (32 rows) of
+//     every query head of the group (or of its share of them, when the heads
+//     are split between workgroups) that can see them.  Q and dO tiles and their rows' statistics stream through
 //     a four-stage LDS ring by the direct-to-LDS load, so three tiles are in
 //     flight while one is computed (a tile is short: 32 MFMAs per wave).  Per
 //     tile S = Q K^T, dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q
