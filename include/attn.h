@@ -39,7 +39,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     never allocates, frees, or synchronises, and keeps no state between calls.
+ *     never allocates, frees, or synchronises, and keeps no state between calls
+ *     (except attn_decode_paged_noalloc, whose scratch is a device-resident
+ *     array of the library: see there).
  *   - Tensors are dense row-major (C order) with the shapes given below.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Work is enqueued asynchronously on it; results are valid once the stream
@@ -294,6 +296,30 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           int N, int Hq, int Hkv, int d, int page, int num_pages,
                           int max_blocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_noalloc -- attn_decode_paged without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Every argument, requirement and result is as for attn_decode_paged (bf16
+ * pages); the same kernels run, with their scratch in a device-resident array
+ * of the library instead of caller memory: 17,432,576 bytes on each device
+ * the library runs on, held until the process ends, enough for
+ * N * Hq <= 65536 (a larger N * Hq returns ATTN_EINVAL).  The call allocates
+ * nothing.  Its first call on a device looks up that device's copy of the
+ * array (an error there returns ATTN_EHIP).  The kernels run on the device
+ * of `stream` (NULL: the calling thread's current device).  Every call on a
+ * device shares that device's array: two calls that overlap in time on one
+ * device race and their results are undefined; calls ordered on one stream
+ * (or otherwise ordered) are safe.  Nothing in the array needs clearing
+ * between calls.
+ */
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens,
+                              void* o, float* lse,
+                              int N, int Hq, int Hkv, int d, int page, int num_pages,
+                              int max_blocks, float scale, int dtype, void* stream);
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid):
  * r(N * Hq * 8) (which workers hold each sequence's pieces)

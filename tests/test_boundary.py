@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
-                                     "attn_decode_paged_fp8", "attn_decode_workspace_size",
+                                     "attn_decode_paged_fp8", "attn_decode_paged_noalloc",
+                                     "attn_decode_workspace_size",
                                      "attn_fwd", "attn_fwd_window", "attn_last_error",
                                      "attn_prefill_paged", "attn_status_string"]
 
@@ -267,6 +268,34 @@ def _dec(**kw):
 def test_decode_rejects_bad_arguments(bad, code):
     assert _dec(**bad) == code
     assert tea.attn_last_error().startswith("attn_decode_paged")
+
+
+def _dec_na(**kw):
+    a = dict(DEC_OK)
+    a.update(kw)
+    return tea.lib().attn_decode_paged_noalloc(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["o"],
+                                               a["lse"], a["N"], a["Hq"], a["Hkv"], a["d"],
+                                               a["page"], a["num_pages"], a["max_blocks"],
+                                               a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), ATTN_EINVAL), (dict(lens=None), ATTN_EINVAL), (dict(N=0), ATTN_EINVAL),
+    (dict(Hq=12, Hkv=5), ATTN_EINVAL), (dict(scale=float("nan")), ATTN_EINVAL),
+    (dict(dtype=ATTN_F32), ATTN_EUNSUPPORTED), (dict(page=32), ATTN_EUNSUPPORTED),
+    (dict(d=96), ATTN_EUNSUPPORTED), (dict(q=P + 4), ATTN_EINVAL),
+    (dict(o=P), ATTN_EINVAL), (dict(lse=6 * P + 64), ATTN_EINVAL),
+    (dict(N=5462, Hq=12, Hkv=2), ATTN_EINVAL),      # N*Hq = 65544 rows: more than the scratch holds
+    (dict(N=65535, Hq=16, Hkv=16), ATTN_EINVAL),
+])
+def test_decode_noalloc_rejects_bad_arguments(bad, code):
+    assert _dec_na(**bad) == code
+    assert tea.attn_last_error().startswith("attn_decode_paged_noalloc")
+
+
+def test_decode_noalloc_names_the_scratch_limit():
+    assert _dec_na(N=5462, Hq=12, Hkv=2) == ATTN_EINVAL
+    assert "scratch" in tea.attn_last_error() and "65536" in tea.attn_last_error()
 
 
 def _dec8(k_scale=0.03, v_scale=0.03, **kw):

@@ -80,6 +80,9 @@ def lib() -> ctypes.CDLL:
     L.attn_prefill_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
                                      i32, i32, f32, i32, i32, vp]
     L.attn_prefill_paged.restype = i32
+    L.attn_decode_paged_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32,
+                                            i32, i32, f32, i32, vp]
+    L.attn_decode_paged_noalloc.restype = i32
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, i32, f32, vp, sz, vp]
     L.attn_decode_paged_fp8.restype = i32
@@ -246,6 +249,33 @@ def attn_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: f
                                  N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
                                  float(scale), _dtype_code(q), workspace.data_ptr(), ws_bytes,
                                  _stream_ptr(q.device, stream))
+    _check(st)
+
+
+def attn_decode_paged_noalloc(q, k_pool, v_pool, block_table, seq_lens, o, lse, scale: float,
+                              page: int = PAGE, stream=None) -> None:
+    """Enqueue attn_decode_paged_noalloc on ``stream``: attn_decode_paged with
+    its scratch in the library's device-resident array (no workspace; calls
+    that overlap in time on one device race).  Arguments as for
+    attn_decode_paged without ``workspace``."""
+    import torch
+    _require_device_tensors(q, k_pool, v_pool, block_table, seq_lens, o, lse)
+    N, Hq, d = q.shape
+    num_pages, Hkv = k_pool.shape[0], k_pool.shape[1]
+    if k_pool.shape != (num_pages, Hkv, page, d) or v_pool.shape != k_pool.shape:
+        raise ValueError("pools must be [num_pages, Hkv, page, d]")
+    if o.shape != q.shape or block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("shape mismatch among q, o, block_table")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (N,):
+        raise TypeError("block_table and seq_lens must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
+        raise ValueError("lse must be float32 [N, Hq]")
+    st = lib().attn_decode_paged_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                         block_table.data_ptr(), seq_lens.data_ptr(), o.data_ptr(),
+                                         lse.data_ptr() if lse is not None else None,
+                                         N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
+                                         float(scale), _dtype_code(q),
+                                         _stream_ptr(q.device, stream))
     _check(st)
 
 

@@ -271,7 +271,7 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
                   float k_scale, float v_scale, const int32_t* block_table,
                   const int32_t* seq_lens, void* o, float* lse, int N, int Hq, int Hkv, int d,
                   int page, int num_pages, int max_blocks, float scale, int dtype,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
     return fail(ATTN_EINVAL, "%s: tensor pointers must be non-NULL", fn);
   if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1 || max_blocks < 1 || page < 1)
@@ -299,10 +299,19 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
   if ((int64_t)N * Hkv * ((max_blocks + 1) / 2) > 0x7fffffff)
     return fail(ATTN_EINVAL, "%s: too many page pairs (N*Hkv*max_blocks/2 >= 2^31)", fn);
   const WsLayout lay = decode_workspace_layout(N, Hq, d);
-  if (!workspace || workspace_bytes < lay.total)
-    return fail(ATTN_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
-                workspace_bytes);
-  if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "%s: misaligned workspace", fn);
+  if (noalloc) {
+    if (workspace != nullptr || workspace_bytes != 0)
+      return fail(ATTN_EINVAL, "%s: takes no workspace", fn);
+    if ((int64_t)N * Hq > attn::kDecodeScratchMaxRows || lay.total > attn::kDecodeScratchBytes)
+      return fail(ATTN_EINVAL,
+                  "%s: N*Hq=%lld exceeds the %lld rows the static scratch (%zu bytes) holds", fn,
+                  (long long)N * Hq, attn::kDecodeScratchMaxRows, attn::kDecodeScratchBytes);
+  } else {
+    if (!workspace || workspace_bytes < lay.total)
+      return fail(ATTN_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, lay.total,
+                  workspace_bytes);
+    if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "%s: misaligned workspace", fn);
+  }
   {
     const size_t es = fp8 ? 1 : 2;
     const size_t qb = (size_t)N * Hq * d * 2, pb = (size_t)num_pages * Hkv * kPage * d * es;
@@ -311,7 +320,7 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
     const void* ins[] = {q, k_pool, v_pool, block_table, seq_lens};
     const size_t in_bytes[] = {qb, pb, pb, btb, nb};
     void* outs[] = {o, lse, workspace};
-    const size_t out_bytes[] = {qb, lb, lay.total};
+    const size_t out_bytes[] = {qb, lb, noalloc ? 0 : lay.total};
     for (int a = 0; a < 3; ++a) {
       for (int i = 0; i < 5; ++i)
         if (overlap(outs[a], out_bytes[a], ins[i], in_bytes[i]))
@@ -322,6 +331,11 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
     }
   }
 
+  if (noalloc) {
+    hipError_t e = attn::decode_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess)
+      return fail(ATTN_EHIP, "%s: static scratch: %s", fn, hipGetErrorString(e));
+  }
   char* ws = static_cast<char*>(workspace);
   attn::DecodeWorkspace dw;
   dw.seg_waves = reinterpret_cast<int2*>(ws);
@@ -347,6 +361,15 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
   return decode_common("attn_decode_paged", false, q, k_pool, v_pool, 1.f, 1.f, block_table,
                        seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks, scale, dtype,
                        workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                              const int32_t* block_table, const int32_t* seq_lens, void* o,
+                              float* lse, int N, int Hq, int Hkv, int d, int page, int num_pages,
+                              int max_blocks, float scale, int dtype, void* stream) {
+  return decode_common("attn_decode_paged_noalloc", false, q, k_pool, v_pool, 1.f, 1.f,
+                       block_table, seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks,
+                       scale, dtype, nullptr, 0, stream, true);
 }
 
 int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool, float k_scale,

@@ -39,6 +39,7 @@
 // All Hq/Hkv query heads of a KV head are the 16 columns of a 16x16x32 MFMA.
 // Positions at or past the sequence length, and pages outside
 // [0, num_pages), are masked and never dereferenced.
+#include <mutex>
 #include <type_traits>
 
 #include "cdna4.hpp"
@@ -595,6 +596,46 @@ hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate.  attn_decode_paged_noalloc runs
+// the same two kernels with their workspace in this array instead of caller
+// memory.  Each device holds its own copy until the process ends; in host
+// code `scratch` names a host-side stand-in, so only the address that
+// hipGetSymbolAddress returns for a device is ever handed to a kernel.  Calls
+// that overlap in time on one device share the array and race.  Nothing in it
+// needs clearing between calls: every entry the combine reads is written by
+// the stream kernel of the same call.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+hipError_t decode_scratch(hipStream_t stream, void** ptr) {
+  int dev = 0;
+  hipError_t e = stream == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* table[kMaxScratchDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (table[dev] == nullptr) {
+    int cur = 0;
+    e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    table[dev] = p;
+  }
+  *ptr = table[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* seq_lens, void* o,

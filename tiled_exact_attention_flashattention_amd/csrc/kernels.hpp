@@ -54,6 +54,20 @@ struct DecodeWorkspace {
   float* lse_part;                   // [2 * kDecodeWaves][kDecodeMaxG]
 };
 
+// Device-resident decode scratch for attn_decode_paged_noalloc: a
+// file-scope array in decode_paged.hip, one copy per device, large enough
+// for the workspace layout of N * Hq <= kDecodeScratchMaxRows at d <= 128.
+constexpr long long kDecodeScratchMaxRows = 65536;
+constexpr size_t kDecodeScratchBytes =
+    (size_t)kDecodeScratchMaxRows * 8 + (size_t)2 * kDecodeWaves * kDecodeMaxG * 128 * 4 +
+    (size_t)2 * kDecodeWaves * kDecodeMaxG * 4;
+static_assert(kDecodeScratchBytes % 256 == 0, "each region of the layout is a multiple of 256");
+
+// Device address of that scratch on the device `stream` runs on (null: the
+// calling thread's current device), looked up once per device with that
+// device current.
+hipError_t decode_scratch(hipStream_t stream, void** ptr);
+
 // fp8: pools hold E4M3 codes; scale_log2 then includes the key scale and
 // v_scale multiplies the output (ignored for bf16 pools).
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
