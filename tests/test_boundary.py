@@ -342,3 +342,46 @@ def test_one_hip_runtime_per_process():
     import tiled_exact_attention_flashattention_amd._binding as b
     tea.lib()
     assert len(b.hip_runtimes_loaded()) == 1, b.hip_runtimes_loaded()
+
+
+_EHIP_CHILD = r"""
+import sys
+sys.path.insert(0, sys.argv[1])
+import torch
+if torch.cuda.device_count() != 0:      # a visible device: never call with fake pointers
+    print("DEVICE_VISIBLE")
+    sys.exit(0)
+import tiled_exact_attention_flashattention_amd as tea
+L = tea.lib()
+P = 1 << 20
+out = []
+# arguments that pass every host check, so the call reaches the HIP launch
+out.append(L.attn_fwd(P, 2 * P, 3 * P, 4 * P, 5 * P, 1, 4, 2, 64, 64, 64, 0.125, 1, 1, None))
+out.append(tea.attn_last_error())
+ws = tea.attn_decode_workspace_size(8, 12, 128, 64, 16)
+out.append(L.attn_decode_paged(P, 2 * P, 3 * P, 4 * P, 5 * P, 6 * P, 7 * P, 8, 12, 2, 128, 16, 100,
+                               64, 0.088, 1, 8 * P, ws, None))
+out.append(tea.attn_last_error())
+print(repr(out))
+"""
+
+
+def test_hip_failure_surfaces_as_ehip():
+    """With no device visible to HIP, a call whose arguments pass every host
+    check fails at the launch: it must return ATTN_EHIP with the runtime's
+    message, never crash or fall back.  Run in a child process whose HIP sees
+    no device, so nothing reaches a GPU even on a GPU host."""
+    import subprocess
+    import sys
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="99", ROCR_VISIBLE_DEVICES="99",
+               CUDA_VISIBLE_DEVICES="99")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _EHIP_CHILD, root], env=env, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    if r.stdout.strip().endswith("DEVICE_VISIBLE"):
+        pytest.skip("HIP still sees a device with HIP_VISIBLE_DEVICES=99")
+    import ast
+    fwd_rc, fwd_msg, dec_rc, dec_msg = ast.literal_eval(r.stdout.strip().splitlines()[-1])
+    assert fwd_rc == 3 and fwd_msg.startswith("attn_fwd: "), (fwd_rc, fwd_msg)
+    assert dec_rc == 3 and dec_msg.startswith("attn_decode_paged: "), (dec_rc, dec_msg)

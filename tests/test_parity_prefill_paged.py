@@ -5,10 +5,9 @@ Small cases cover ragged chunk and context lengths, chunks that fill the
 whole context, one-token chunks, the sliding window, poisoned (NaN) slots
 past each sequence's end, GQA ratios and both head sizes; a chunk equal to
 the whole sequence must reproduce attn_fwd on the contiguous keys bit for
-bit.  Sequences are dispatched longest first by a rank the kernel computes
-from the lengths (up to 256 sequences, ties by index, in the given order
-above that): equal lengths and more than 256 sequences must still give every
-sequence its own workgroups.  The full-size chunked workload (16 sequences,
+bit.  Sequences are dispatched longest first by a selection the kernel makes
+from the lengths (ties by index): equal lengths and many sequences must
+still give every sequence its own workgroups.  The full-size chunked workload (16 sequences,
 512-token chunks, up to 8192 cached tokens) is compared on sampled rows in
 the configuration the benchmark times.
 """
@@ -25,14 +24,14 @@ torch = pytest.importorskip("torch")
 tea = pytest.importorskip("tiled_exact_attention_flashattention_amd")
 
 
-def _run(inp):
+def _run(inp, fill=7.0):
     dev = "cuda"
     q, kp, vp = (t.to(dev) for t in (inp.q, inp.k_pool, inp.v_pool))
     bt = torch.from_numpy(inp.block_table).to(dev)
     sl = torch.from_numpy(inp.seq_lens).to(dev)
     ql = torch.from_numpy(inp.q_lens).to(dev)
-    o = torch.full_like(q, 7.0)                     # rows past q_lens must stay 7
-    lse = torch.full((inp.N, inp.Hq, inp.T), 7.0, dtype=torch.float32, device=dev)
+    o = torch.full_like(q, fill)                    # rows past q_lens must keep the fill
+    lse = torch.full((inp.N, inp.Hq, inp.T), fill, dtype=torch.float32, device=dev)
     tea.attn_prefill_paged(q, kp, vp, bt, sl, ql, o, lse, inp.scale, window=inp.window)
     torch.cuda.synchronize()
     return o, lse
@@ -128,23 +127,29 @@ def test_equal_lengths_each_sequence_computed_once():
     _check(inp, name, o, lse)
 
 
-def test_more_sequences_than_the_device_ranking_covers():
-    name = "pp_many"
-    inp = workloads.make_prefill_paged(300, 2, 1, 8, 64, 1, 64, seed=seed_of(name),
+@pytest.mark.parametrize("N", [256, 300, 1000, 1100])
+def test_many_sequences_each_get_their_workgroups(N):
+    """The longest-first dispatch selects every sequence exactly once at any N
+    (the selection reads the lengths in passes over all N)."""
+    name = f"pp_many_{N}"
+    inp = workloads.make_prefill_paged(N, 2, 1, 8, 64, 1, 64, seed=seed_of(name),
                                        poison_tail=True, extra_pages=3, name=name)
-    announce(f"attn_prefill_paged {name}: N=300 Hq=2 Hkv=1 T=8 d=64")
+    announce(f"attn_prefill_paged {name}: N={N} Hq=2 Hkv=1 T=8 d=64")
     o, lse = _run(inp)
     _check(inp, name, o, lse)
 
 
 def test_chunked_prefill_6_sampled():
+    """Sampled rows of every sequence and head, outputs NaN-filled: a row the
+    kernel never wrote cannot pass (every row is below q_lens here)."""
     inp = workloads.chunked_prefill_6()
-    announce("attn_prefill_paged chunked_prefill_6 full size, sampled rows")
-    o, lse = _run(inp)
+    assert (inp.q_lens == inp.T).all()
+    announce("attn_prefill_paged chunked_prefill_6 full size, sampled rows of every sequence")
+    o, lse = _run(inp, fill=float("nan"))
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), "unwritten rows"
     rng = np.random.default_rng(seed_of("cp6"))
 
     def rows_of(n, Tn):
         return np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, Tn - 2, Tn - 1],
-                                         rng.integers(0, Tn, 24)]))
-    _check(inp, "chunked_prefill_6", o, lse, seqs=[0, 5, 15], rows_of=rows_of)
-    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+                                         rng.integers(0, Tn, 16)]))
+    _check(inp, "chunked_prefill_6", o, lse, seqs=range(inp.N), rows_of=rows_of)

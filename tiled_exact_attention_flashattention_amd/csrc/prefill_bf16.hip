@@ -85,8 +85,110 @@ __device__ __forceinline__ int v_swz(int row) { return D == 128 ? 2 * (row & 7) 
 constexpr int kXcdCount = 8;
 constexpr int kCusPerXcd = 32;
 
-// Chunked prefill: sequences are ranked by length on the device up to this count.
-constexpr int kSortMax = 256;
+// Chunked prefill: the index of the slot-th longest of the n sequences
+// (lengths clamped to [0, lmax], ties by index), found by every thread of the
+// workgroup.  The keys ~len of the first kSelCache sequences are staged in LDS
+// by one coalesced pass.  Up to NT sequences, thread c counts the keys below
+// its own (a rank, ties by index) and the thread whose rank is `slot` names
+// itself.  Beyond that, radix selection on the key in four 8-bit digits, from
+// the top: a histogram of the digit over the sequences that match the digits
+// fixed so far locates the digit of the wanted rank and the rank left within
+// it; the sequences with the selected length are then counted in index order
+// to pick the remaining rank.  Each pass reads the n keys once, so the cost
+// grows linearly with n.
+constexpr int kSelCache = 1024;
+
+template <int NT>
+__device__ __forceinline__ int select_by_length(const int32_t* __restrict__ lens, int n, int lmax,
+                                                int slot) {
+  static_assert(NT % 64 == 0 && NT >= 256, "one wave scans 256 bins; a lane covers NT/64 counts");
+  __shared__ unsigned cache[kSelCache];
+  __shared__ unsigned hist[256];
+  __shared__ unsigned sh_prefix, sh_rank;
+  __shared__ unsigned sh_cnt[NT];
+  const int tid = threadIdx.x, lane = tid & 63;
+  auto load_key = [&](int c) { return ~(unsigned)min(max(lens[c], 0), lmax); };
+  for (int c = tid; c < min(n, kSelCache); c += NT) cache[c] = load_key(c);
+  __syncthreads();
+  auto key = [&](int c) { return c < kSelCache ? cache[c] : load_key(c); };
+  if (n <= NT) {
+    if (tid < n) {
+      const unsigned u = cache[tid];
+      int rk = 0;
+      for (int t = 0; t < n; ++t) {
+        const unsigned x = cache[t];
+        rk += (x < u) || (x == u && t < tid);
+      }
+      if (rk == slot) sh_prefix = (unsigned)tid;
+    }
+    __syncthreads();
+    return (int)sh_prefix;
+  }
+  // Wave 0: of the counts v[0 .. per*64) (per consecutive ones a lane), the
+  // position p where the running sum first exceeds `rank`, and the sum before it.
+  auto find = [&](const unsigned* v, int per, unsigned rank, unsigned& before) {
+    unsigned own = 0;
+    for (int e = 0; e < per; ++e) own += v[per * lane + e];
+    unsigned incl = own;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const unsigned y = __shfl_up(incl, m);
+      if (lane >= m) incl += y;
+    }
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(incl > rank);
+    const int L = hit ? __builtin_ctzll(hit) : 63;
+    unsigned cum = __shfl(incl - own, L);
+    int p = per * L;
+    for (int e = 0; e < per - 1; ++e, ++p) {
+      const unsigned x = v[p];
+      if (cum + x > rank) break;
+      cum += x;
+    }
+    before = cum;
+    return p;
+  };
+  unsigned prefix = 0, mask = 0, rank = (unsigned)slot;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += NT) hist[i] = 0;
+    __syncthreads();
+    for (int c = tid; c < n; c += NT) {
+      const unsigned u = key(c);
+      if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      unsigned cum;
+      const int d = find(hist, 4, rank, cum);
+      if (lane == 0) {
+        sh_prefix = prefix | ((unsigned)d << shift);
+        sh_rank = rank - cum;
+      }
+    }
+    __syncthreads();
+    prefix = sh_prefix;
+    rank = sh_rank;
+    mask |= 255u << shift;
+    __syncthreads();
+  }
+  // the rank-th (in index order) sequence whose key equals prefix
+  const int chunk = (n + NT - 1) / NT, c0 = tid * chunk, c1 = min(n, c0 + chunk);
+  unsigned cnt = 0;
+  for (int c = c0; c < c1; ++c) cnt += key(c) == prefix;
+  sh_cnt[tid] = cnt;
+  __syncthreads();
+  if (tid < 64) {
+    unsigned before;
+    const int t = find(sh_cnt, NT / 64, rank, before);
+    if (lane == 0) {
+      int c = t * chunk;
+      for (unsigned seen = before;; ++c)
+        if (key(c) == prefix && seen++ == rank) break;
+      sh_prefix = (unsigned)c;
+    }
+  }
+  __syncthreads();
+  return (int)sh_prefix;
+}
 
 // Slack of the running maximum (log2 units): P = exp2(s - m) may reach
 // 2^kLazyTau, far inside bf16 and fp32 range.
@@ -129,10 +231,9 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   int hgi, grp, rank;
   if (PAGED) {
     // Chunked prefill: a sequence's work grows with its cached length, so
-    // sequences are dispatched longest first (workgroups [slot W, (slot+1) W)
-    // take the slot-th longest, ties by index; with more than kSortMax
-    // sequences the given order is kept).  Every workgroup ranks the same
-    // lengths, so all agree on the order.
+    // sequences are dispatched longest first: workgroups [slot W, (slot+1) W)
+    // take the slot-th longest (ties by index).  Every workgroup selects that
+    // sequence itself from the same lengths, so all agree on the order.
     // The first two rounds of the dispatch put workgroups pid and pid + 256
     // on one CU (the first 512 ids fill two slots of each of the 256 CUs):
     // ids 256..511 take the lightest items, in reverse, so that each CU
@@ -146,22 +247,11 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     hgi = w % hpg;
     const int r = w / hpg;
     rank = r / Hkv;
-    int bsel = slot;
-    if (B <= kSortMax) {
-      __shared__ int sel;
-      for (int cand = threadIdx.x; cand < B; cand += kThreads) {
-        const int lc = pkv.seq_lens[cand];
-        int rk = 0;
-        for (int t = 0; t < B; ++t) {
-          const int lt = pkv.seq_lens[t];
-          rk += (lt > lc) || (lt == lc && t < cand);
-        }
-        if (rk == slot) sel = cand;
-      }
-      __syncthreads();
-      bsel = sel;
-    }
-    grp = bsel * Hkv + r % Hkv;
+    __shared__ int sel;
+    const int chosen = select_by_length<kThreads>(pkv.seq_lens, B, pkv.max_blocks * 16, slot);
+    if (threadIdx.x == 0) sel = chosen;
+    __syncthreads();
+    grp = sel * Hkv + r % Hkv;
   } else if ((G & 7) == 0) {
     // XCD pid%8 walks its own eighth of the groups: [tile rank][group][head].
     int s = pid >> 3;
