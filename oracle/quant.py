@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for attention over fp8-quantised KV pages.
+"""Float64 CPU oracle for attention over 8-bit quantised KV pages (fp8, int8).
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import or run anything in ``oracle/``.
@@ -15,6 +15,10 @@ design notes) is:
   the largest finite magnitude is 448;
 * one float scale per tensor: K = k_scale * e4m3(k_code), V likewise;
 * attention is then the plain definition on the dequantised values.
+
+The integer reading (also listed in the design notes): int8 pages hold
+signed two's-complement bytes, -128 .. 127, with one float scale per tensor,
+K = k_scale * code and V = v_scale * code (symmetric quantisation).
 """
 from __future__ import annotations
 
@@ -43,4 +47,22 @@ def decode_paged_fp8(q, k_codes, v_codes, k_scale, v_scale, block_table, seq_len
                      page=16, seqs=None):
     """decode_paged on the dequantised pools (codes [num_pages,Hkv,page,d] uint8)."""
     return decode_paged(q, dequantise(k_codes, k_scale), dequantise(v_codes, v_scale),
+                        block_table, seq_lens, scale, page=page, seqs=seqs)
+
+
+def int8_to_float(codes) -> np.ndarray:
+    """Value of each byte read as a signed two's-complement integer, float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(c >= 128, c - 256, c).astype(np.float64)
+
+
+def dequantise_int8(codes, scale) -> np.ndarray:
+    """scale * int8(code), float64."""
+    return float(scale) * int8_to_float(codes)
+
+
+def decode_paged_int8(q, k_codes, v_codes, k_scale, v_scale, block_table, seq_lens, scale,
+                      page=16, seqs=None):
+    """decode_paged on the dequantised pools (codes [num_pages,Hkv,page,d] bytes)."""
+    return decode_paged(q, dequantise_int8(k_codes, k_scale), dequantise_int8(v_codes, v_scale),
                         block_table, seq_lens, scale, page=page, seqs=seqs)

@@ -239,3 +239,67 @@ def test_fp8_single_code_value_cache():
     vc[:] = 0x38
     o, _ = oracle.decode_paged_fp8(q, kc, vc, 0.05, 0.75, bt, lens, 0.3)
     np.testing.assert_allclose(o, 0.75, rtol=1e-14, atol=1e-14)
+
+
+# --- int8 pages ------------------------------------------------------------------
+
+def test_int8_closed_forms():
+    f = oracle.int8_to_float
+    assert list(f([0x00, 0x01, 0x7F, 0x80, 0x81, 0xFE, 0xFF])) == [0, 1, 127, -128, -127, -2, -1]
+
+
+def test_int8_all_codes_match_numpy_view():
+    codes = np.arange(256, dtype=np.uint8)
+    np.testing.assert_array_equal(oracle.int8_to_float(codes),
+                                  codes.view(np.int8).astype(np.float64))
+
+
+def _int8_case(name):
+    q, kc, vc, bt, lens = _fp8_case(name)       # any bytes are valid int8 codes
+    return q, kc, vc, bt, lens
+
+
+def test_int8_value_scale_scales_the_output():
+    q, kc, vc, bt, lens = _int8_case("i8v")
+    o1, l1 = oracle.decode_paged_int8(q, kc, vc, 0.01, 1.0, bt, lens, 0.3)
+    o2, l2 = oracle.decode_paged_int8(q, kc, vc, 0.01, 0.125, bt, lens, 0.3)
+    np.testing.assert_allclose(o2, 0.125 * o1, rtol=1e-14, atol=1e-14)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_int8_key_scale_is_a_softmax_temperature():
+    q, kc, vc, bt, lens = _int8_case("i8k")
+    o1, l1 = oracle.decode_paged_int8(q, kc, vc, 0.02, 0.5, bt, lens, 0.3)
+    o2, l2 = oracle.decode_paged_int8(q, kc, vc, 1.0, 0.5, bt, lens, 0.3 * 0.02)
+    np.testing.assert_allclose(o1, o2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=1e-12, atol=1e-13)
+
+
+def test_int8_constant_value_cache_and_zero_keys():
+    """V codes all -3: O = -3 v_scale.  K codes all 0: every logit is 0, so the
+    LSE is ln(length) and O is the mean of the visible values."""
+    q, kc, vc, bt, lens = _int8_case("i8c")
+    vc2 = np.full_like(vc, 0xFD)                                  # -3
+    o, _ = oracle.decode_paged_int8(q, kc, vc2, 0.05, 0.75, bt, lens, 0.3)
+    np.testing.assert_allclose(o, -2.25, rtol=1e-14, atol=1e-14)
+    kz = np.zeros_like(kc)
+    o, lse = oracle.decode_paged_int8(q, kz, vc, 0.05, 0.5, bt, lens, 0.3)
+    np.testing.assert_allclose(lse, np.log(lens.astype(np.float64))[:, None] * np.ones(q.shape[1]),
+                               rtol=1e-14, atol=1e-14)
+    vals = oracle.int8_to_float(vc) * 0.5
+    for n in range(len(lens)):
+        L = int(lens[n])
+        for h in range(q.shape[1]):
+            hk = h // (q.shape[1] // kc.shape[1])
+            rows = [vals[bt[n, t // 16], hk, t % 16] for t in range(L)]
+            np.testing.assert_allclose(o[n, h], np.mean(rows, axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_int8_sign_mistake_is_caught():
+    """A reading of the bytes as unsigned changes the result (the pins above see it)."""
+    q, kc, vc, bt, lens = _int8_case("i8s")
+    kc = kc | 0x80                                                # every key code negative
+    o_s, _ = oracle.decode_paged_int8(q, kc, vc, 0.05, 0.5, bt, lens, 0.3)
+    o_u, _ = oracle.decode_paged(q, 0.05 * kc.astype(np.float64), 0.5 * vc.astype(np.float64), bt,
+                                 lens, 0.3)
+    assert np.abs(o_s - o_u).max() > 1e-3

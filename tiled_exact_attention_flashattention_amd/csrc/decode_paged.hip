@@ -517,13 +517,17 @@ void decode_combine_kernel(const int32_t* __restrict__ seq_lens, const int2* __r
   const int G = Hq / Hkv, hk = h / G, hh = h - hk * G;
   const int lane = threadIdx.x;
   bf16* orow = o + (size_t)nh * D + lane * PER;
-  if (clamp_len(seq_lens[n], max_blocks) == 0) {
+  // both loads in one round trip (a segment's entry is only meaningful, and
+  // only used, when the sequence is not empty)
+  const int len = seq_lens[n];
+  const int2 ws = seg_waves[(size_t)n * Hkv + hk];
+  asm volatile("" ::"s"(len), "s"(ws.x), "s"(ws.y));   // (kept ahead of the branch)
+  if (clamp_len(len, max_blocks) == 0) {
 #pragma unroll
     for (int e = 0; e < PER; ++e) orow[e] = (bf16)0.f;
     if (lse != nullptr && lane == 0) lse[nh] = -INFINITY;
     return;
   }
-  const int2 ws = seg_waves[(size_t)n * Hkv + hk];
   if (ws.x == ws.y) return;                   // finished in place
   if (ws.x < 0 || ws.y < ws.x || ws.y >= kDecodeWaves) return;   // never written: not ours
   const int npieces = ws.y - ws.x + 1;

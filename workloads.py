@@ -269,7 +269,8 @@ def make_prefill_paged(N, Hq, Hkv, T, d, min_len, max_len, q_lens=None, lens=Non
 
 @dataclass
 class DecodeFp8Inputs:
-    """Paged decode with E4M3 key/value pages (codes as uint8) and per-tensor scales."""
+    """Paged decode with 8-bit key/value pages (E4M3 or int8 codes as uint8
+    bytes) and per-tensor scales."""
     N: int
     Hq: int
     Hkv: int
@@ -330,6 +331,49 @@ def make_decode_fp8(N, Hq, Hkv, d, min_len, max_len, page=PAGE, max_blocks=None,
                            kc, vc, name=name)
 
 
+def make_decode_int8(N, Hq, Hkv, d, min_len, max_len, page=PAGE, max_blocks=None, seed=0,
+                     k_scale=2.0 ** -5, v_scale=2.0 ** -5, poison_tail=False, lens=None, name=""):
+    """The draws of ``make_decode`` (same order and seed use), then K and V
+    quantised symmetrically to int8 codes: value / scale rounded to nearest
+    even and clipped to [-127, 127] (N(0,1) draws at the default scale 2^-5
+    clip beyond 3.97).  Codes are stored as their two's-complement bytes
+    (torch uint8).  ``poison_tail`` writes the code -128 into the unused slots
+    of every last page (never used by a correct kernel)."""
+    import torch
+    rng = np.random.default_rng(seed)
+    drawn = rng.integers(min_len, max_len + 1, N)
+    seq_lens = np.asarray(drawn if lens is None else lens, dtype=np.int64)
+    pages_per = (seq_lens + page - 1) // page
+    if max_blocks is None:
+        max_blocks = int((max_len + page - 1) // page)
+    P = int(pages_per.sum())
+    perm = rng.permutation(P)
+    block_table = np.full((N, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for n in range(N):
+        cnt = int(pages_per[n])
+        block_table[n, :cnt] = perm[off:off + cnt]
+        off += cnt
+    q = rng.standard_normal((N, Hq, d), dtype=np.float32)
+    k = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+    v = rng.standard_normal((P, Hkv, page, d), dtype=np.float32)
+
+    def codes(x, sc):
+        c = np.clip(np.rint(x / np.float32(sc)), -127, 127).astype(np.int8)
+        return torch.from_numpy(c.view(np.uint8).copy())
+    kc, vc = codes(k, k_scale), codes(v, v_scale)
+    if poison_tail:
+        for n in range(N):
+            used = int(seq_lens[n]) - (int(pages_per[n]) - 1) * page
+            if used < page:
+                last = block_table[n, int(pages_per[n]) - 1]
+                kc[last, :, used:, :] = 0x80
+                vc[last, :, used:, :] = 0x80
+    return DecodeFp8Inputs(N, Hq, Hkv, d, page, P, max_blocks, 1.0 / math.sqrt(d), float(k_scale),
+                           float(v_scale), seq_lens.astype(np.int32), block_table, _cast(q, "bf16"),
+                           kc, vc, name=name)
+
+
 # --- the five named workloads -------------------------------------------------
 
 def prefill_1():
@@ -368,6 +412,13 @@ def decode_fp8_7(poison_tail=False):
                            poison_tail=poison_tail, name="decode_fp8_7")
 
 
+def decode_int8_8(poison_tail=False):
+    """decode_5's shape (64 sequences, lengths U[512, 8192], Hq=12, Hkv=2,
+    d=128, 16-token pages) with int8 key/value pages."""
+    return make_decode_int8(64, 12, 2, 128, 512, 8192, page=PAGE, max_blocks=512, seed=1008,
+                            poison_tail=poison_tail, name="decode_int8_8")
+
+
 def backward_3():
     """The gradient pass of prefill_3 (same q, k, v), dO drawn after v."""
     return make_backward(4, 12, 2, 4096, 4096, 128, causal=True, seed=1003, name="backward_3")
@@ -382,6 +433,7 @@ WORKLOADS = {
     "backward_3": backward_3,
     "chunked_prefill_6": chunked_prefill_6,
     "decode_fp8_7": decode_fp8_7,
+    "decode_int8_8": decode_int8_8,
 }
 
 # Human-readable shapes, used for labels in the benchmark output.
@@ -396,4 +448,6 @@ SHAPES = {
                               max_len=8192, dtype="bf16"),
     "decode_fp8_7": dict(N=64, Hq=12, Hkv=2, d=128, page=16, min_len=512, max_len=8192,
                          dtype="bf16 q, e4m3 kv"),
+    "decode_int8_8": dict(N=64, Hq=12, Hkv=2, d=128, page=16, min_len=512, max_len=8192,
+                          dtype="bf16 q, int8 kv"),
 }
