@@ -37,10 +37,13 @@ Reported (one JSON line on stdout):
                       d=128, keys through the block table;
   decode_fp8          attn_decode_paged_fp8 on decode_5's shape with E4M3 pages
                       (decode_fp8_7): GB/s over the bytes it must read;
+  decode_int8         attn_decode_paged_int8 on the same shape with int8 pages
+                      (decode_int8_8), likewise;
   backward            the gradient pass attn_bwd on prefill_3's shape,
                       TFLOP/s with FLOPs = 10*d per visible (query, key) pair
                       (recomputed scores, dP, dV, dQ, dK);
-  (window, chunked, decode_fp8 and backward each carry their own cpu_baseline)
+  (window, chunked, decode_fp8, decode_int8 and backward each carry their own
+  cpu_baseline)
   cpu_baseline        the oracle's figure for the headline workload.
 The flush reads sit outside the kernel events but inside ms_per_step.
 
@@ -222,24 +225,27 @@ def bench_chunked(tea, workloads, dev, stream, flush, cpu_budget_s=None):
     return rec
 
 
-def bench_decode_fp8(tea, workloads, dev, stream, flush, cpu_budget_s=None):
-    """attn_decode_paged_fp8 on decode_fp8_7 (stream + combine kernels), and the
-    oracle on sampled sequences."""
+def bench_decode_q8(tea, workloads, dev, stream, flush, cpu_budget_s=None, fmt="fp8"):
+    """attn_decode_paged_fp8 on decode_fp8_7 (E4M3 pages) or attn_decode_paged_int8 on
+    decode_int8_8 (int8 pages): stream + combine kernels, and the oracle on
+    sampled sequences."""
     import torch
-    x = workloads.decode_fp8_7()
+    x = workloads.decode_fp8_7() if fmt == "fp8" else workloads.decode_int8_8()
+    entry = tea.attn_decode_paged_fp8 if fmt == "fp8" else tea.attn_decode_paged_int8
     xq, kc, vc = x.q.to(dev), x.k_codes.to(dev), x.v_codes.to(dev)
     bt, sl = torch.from_numpy(x.block_table).to(dev), torch.from_numpy(x.seq_lens).to(dev)
     xo = torch.empty_like(xq)
     xl = torch.empty((x.N, x.Hq), dtype=torch.float32, device=dev)
     ws = tea.decode_workspace(x.N, x.Hq, x.d, x.max_blocks, dev)
-    ms, n = timed_launches(stream, flush, lambda: tea.attn_decode_paged_fp8(
+    ms, n = timed_launches(stream, flush, lambda: entry(
         xq, kc, vc, x.k_scale, x.v_scale, bt, sl, xo, xl, x.scale, ws, stream=stream), n=12)
     tokens = int(x.seq_lens.astype("int64").sum())
     pages = int(((x.seq_lens.astype("int64") + x.page - 1) // x.page).sum())
     nbytes = tokens * x.Hkv * x.d * 2 + 2 * x.N * x.Hq * x.d * 2 + x.N * x.Hq * 4 + x.N * 4 + pages * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, E4M3 K/V pages, lengths "
-                     f"U[512,8192] (sum {tokens})", "kernel": "decode_stream_kernel<fp8>+"
+    rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, "
+                     f"{'E4M3' if fmt == 'fp8' else 'int8'} K/V pages, lengths "
+                     f"U[512,8192] (sum {tokens})", "kernel": f"decode_stream_kernel<{fmt}>+"
                      "decode_combine_kernel", "ms": ms, "value": gbs, "unit": "GB/s",
            "algorithmic_bytes": nbytes, "bound": "hbm", "peak": PEAK_HBM_GBS,
            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": n,
@@ -251,14 +257,14 @@ def bench_decode_fp8(tea, workloads, dev, stream, flush, cpu_budget_s=None):
         import oracle
         qd = x.q.double().numpy()
         kcodes, vcodes = x.k_codes.numpy(), x.v_codes.numpy()
+        ref = oracle.decode_paged_fp8 if fmt == "fp8" else oracle.decode_paged_int8
 
         def one_sequence(n):
             # the pages sequence n uses, as a pool of their own with the table renumbered
             nb = (int(x.seq_lens[n]) + x.page - 1) // x.page
             pages = x.block_table[n, :nb]
-            oracle.decode_paged_fp8(qd[n:n + 1], kcodes[pages], vcodes[pages], x.k_scale,
-                                    x.v_scale, np.arange(nb, dtype=np.int32)[None, :],
-                                    x.seq_lens[n:n + 1], x.scale, page=x.page)
+            ref(qd[n:n + 1], kcodes[pages], vcodes[pages], x.k_scale, x.v_scale,
+                np.arange(nb, dtype=np.int32)[None, :], x.seq_lens[n:n + 1], x.scale, page=x.page)
 
         done, work, tc = oracle_sample(
             cpu_budget_s, list(range(x.N)), one_sequence,
@@ -266,7 +272,7 @@ def bench_decode_fp8(tea, workloads, dev, stream, flush, cpu_budget_s=None):
         rec["cpu_baseline"] = {"value": work / tc / 1e9, "unit": "GB/s", "cores": blas_threads(),
                                "kind": "oracle",
                                "sample": f"{done} sequences of this workload, one oracle call "
-                                         f"each on the E4M3 pages it uses ({tc:.1f} s)"}
+                                         f"each on the {fmt} pages it uses ({tc:.1f} s)"}
     return rec
 
 
@@ -718,7 +724,8 @@ def main():
             nb_ = None if args.no_cpu_baseline else args.cpu_budget / 5
             out["window"] = bench_window(tea, workloads, dev, stream, flush, nb_)
             out["chunked"] = bench_chunked(tea, workloads, dev, stream, flush, nb_)
-            out["decode_fp8"] = bench_decode_fp8(tea, workloads, dev, stream, flush, nb_)
+            out["decode_fp8"] = bench_decode_q8(tea, workloads, dev, stream, flush, nb_, "fp8")
+            out["decode_int8"] = bench_decode_q8(tea, workloads, dev, stream, flush, nb_, "int8")
         if not args.no_backward:
             out["backward"] = bench_backward(tea, workloads, dev, stream, flush,
                                              None if args.no_cpu_baseline else args.cpu_budget / 3)

@@ -17,6 +17,7 @@
  *                      cache stored in fixed-size pages reached through a
  *                      block table.
  *   attn_decode_paged_fp8  the same over fp8 (E4M3) pages with scales.
+ *   attn_decode_paged_int8 the same over int8 pages with scales.
  *
  * Definitions (page titles and sections of the sources):
  *   - "Advanced Attention Mechanisms - II" (A. Das), section Tiling, steps 1-3:
@@ -296,6 +297,33 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           int N, int Hq, int Hkv, int d, int page, int num_pages,
                           int max_blocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_paged_int8 -- attn_decode_paged over int8 key/value pages.
+ *
+ *   k_pool, v_pool  [num_pages, Hkv, page, d]  8-bit two's-complement integer
+ *                   codes (-128 .. 127, passed as bytes)
+ *   k_scale, v_scale  float  per-tensor scales: K = k_scale * code,
+ *                            V = v_scale * code (symmetric quantisation)
+ *   every other argument as for attn_decode_paged_fp8.
+ *
+ * "Fast attention kernels and operator fusion accelerate AI models",
+ * section on kernel fusion: dequantisation is fused into the matrix product
+ * that consumes it; the integer format and per-tensor scales are our reading.
+ * The codes are widened to bf16 in registers (exactly: every integer in
+ * -128 .. 127 is a bf16 value) right before the MFMAs, k_scale folds into the
+ * logit scale and v_scale into the output normalisation, so the result is
+ * attn_decode_paged's definition on the dequantised cache with half the bytes
+ * per token read from HBM.  Slots past a sequence's length are never used.
+ *
+ * Requirements: as for attn_decode_paged_fp8.
+ */
+int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool,
+                           float k_scale, float v_scale, const int32_t* block_table,
+                           const int32_t* seq_lens, void* o, float* lse,
+                           int N, int Hq, int Hkv, int d, int page, int num_pages,
+                           int max_blocks, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * attn_decode_paged_noalloc -- attn_decode_paged without a workspace argument,

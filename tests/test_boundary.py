@@ -26,7 +26,8 @@ def _declared_functions():
 
 def test_header_declares_the_expected_entry_points():
     assert _declared_functions() == ["attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged",
-                                     "attn_decode_paged_fp8", "attn_decode_paged_noalloc",
+                                     "attn_decode_paged_fp8", "attn_decode_paged_int8",
+                                     "attn_decode_paged_noalloc",
                                      "attn_decode_workspace_size",
                                      "attn_fwd", "attn_fwd_window", "attn_last_error",
                                      "attn_prefill_paged", "attn_status_string"]
@@ -385,3 +386,27 @@ def test_hip_failure_surfaces_as_ehip():
     fwd_rc, fwd_msg, dec_rc, dec_msg = ast.literal_eval(r.stdout.strip().splitlines()[-1])
     assert fwd_rc == 3 and fwd_msg.startswith("attn_fwd: "), (fwd_rc, fwd_msg)
     assert dec_rc == 3 and dec_msg.startswith("attn_decode_paged: "), (dec_rc, dec_msg)
+
+
+def _dec_i8(k_scale=0.03, v_scale=0.03, **kw):
+    a = dict(DEC_OK)
+    a.update(kw)
+    return tea.lib().attn_decode_paged_int8(a["q"], a["k"], a["v"], k_scale, v_scale, a["bt"],
+                                            a["lens"], a["o"], a["lse"], a["N"], a["Hq"], a["Hkv"],
+                                            a["d"], a["page"], a["num_pages"], a["max_blocks"],
+                                            a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("scales,bad,code", [
+    ((0.0, 0.03), {}, ATTN_EINVAL), ((0.03, -1.0), {}, ATTN_EINVAL),
+    ((float("nan"), 0.03), {}, ATTN_EINVAL), ((0.03, float("inf")), {}, ATTN_EINVAL),
+    ((1e38, 0.03), dict(scale=1e3), ATTN_EINVAL),
+    ((0.03, 0.03), dict(q=None), ATTN_EINVAL), ((0.03, 0.03), dict(page=8), ATTN_EUNSUPPORTED),
+    ((0.03, 0.03), dict(d=96), ATTN_EUNSUPPORTED), ((0.03, 0.03), dict(ws_bytes=WS - 1), ATTN_EINVAL),
+    ((0.03, 0.03), dict(v=3 * P + 8), ATTN_EINVAL), ((0.03, 0.03), dict(Hq=34, Hkv=2), ATTN_EUNSUPPORTED),
+    ((0.03, 0.03), dict(ws=2 * P), ATTN_EINVAL),             # workspace over the key pool
+    ((0.03, 0.03), dict(o=P), ATTN_EINVAL),                  # output aliases q
+])
+def test_decode_int8_rejects_bad_arguments(scales, bad, code):
+    assert _dec_i8(*scales, **bad) == code
+    assert tea.attn_last_error().startswith("attn_decode_paged_int8")

@@ -7,7 +7,8 @@ not been built (``python -m tiled_exact_attention_flashattention_amd.build``).
 """
 from ._binding import (ATTN_BF16, ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATTN_F32,
                        ATTN_OK, PAGE, AttnError, attn_bwd, attn_bwd_workspace_size,
-                       attn_decode_paged, attn_decode_paged_fp8, attn_decode_paged_noalloc,
+                       attn_decode_paged, attn_decode_paged_fp8, attn_decode_paged_int8,
+                       attn_decode_paged_noalloc,
                        attn_decode_workspace_size,
                        attn_fwd, attn_fwd_window, attn_last_error, attn_prefill_paged,
                        attn_status_string, bwd, check_paged_inputs, decode_paged,
@@ -16,7 +17,7 @@ from ._binding import (ATTN_BF16, ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATT
 __all__ = [
     "ATTN_BF16", "ATTN_EHIP", "ATTN_EINVAL", "ATTN_EUNSUPPORTED", "ATTN_F32", "ATTN_OK", "PAGE",
     "AttnError", "attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged", "attn_decode_paged_fp8",
-    "attn_decode_paged_noalloc",
+    "attn_decode_paged_int8", "attn_decode_paged_noalloc",
     "attn_decode_workspace_size", "attn_fwd", "attn_fwd_window", "attn_last_error",
     "attn_prefill_paged", "attn_status_string", "bwd", "check_paged_inputs",
     "decode_paged", "decode_workspace", "fwd", "lib", "library_path",

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
     L.attn_decode_paged_fp8.argtypes = [vp, vp, vp, f32, f32, vp, vp, vp, vp, i32, i32, i32, i32,
                                         i32, i32, i32, f32, vp, sz, vp]
     L.attn_decode_paged_fp8.restype = i32
+    L.attn_decode_paged_int8.argtypes = list(L.attn_decode_paged_fp8.argtypes)
+    L.attn_decode_paged_int8.restype = i32
     L.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32,
                            i32, i32, vp, sz, vp]
     L.attn_bwd.restype = i32
@@ -379,6 +381,38 @@ def attn_decode_paged_fp8(q, k_codes, v_codes, k_scale: float, v_scale: float, b
                                      N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
                                      float(scale), workspace.data_ptr(), ws_bytes,
                                      _stream_ptr(q.device, stream))
+    _check(st)
+
+
+def attn_decode_paged_int8(q, k_codes, v_codes, k_scale: float, v_scale: float, block_table,
+                           seq_lens, o, lse, scale: float, workspace, page: int = PAGE,
+                           stream=None) -> None:
+    """Enqueue attn_decode_paged_int8: pools are int8 codes (torch int8 or their
+    uint8 bytes) [num_pages,Hkv,page,d] with per-tensor scales."""
+    import torch
+    _require_device_tensors(q, k_codes, v_codes, block_table, seq_lens, o, lse, workspace)
+    N, Hq, d = q.shape
+    num_pages, Hkv = k_codes.shape[0], k_codes.shape[1]
+    if k_codes.shape != (num_pages, Hkv, page, d) or v_codes.shape != k_codes.shape:
+        raise ValueError("pools must be [num_pages, Hkv, page, d]")
+    if k_codes.dtype not in (torch.int8, torch.uint8) or v_codes.dtype != k_codes.dtype:
+        raise TypeError("int8 pools must be int8 codes (or their uint8 bytes)")
+    if o.shape != q.shape or block_table.dim() != 2 or block_table.shape[0] != N:
+        raise ValueError("shape mismatch among q, o, block_table")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32 or seq_lens.shape != (N,):
+        raise TypeError("block_table and seq_lens must be int32")
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != (N, Hq)):
+        raise ValueError("lse must be float32 [N, Hq]")
+    if q.dtype != torch.bfloat16 or o.dtype != torch.bfloat16:
+        raise TypeError("q and o must be bfloat16")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_decode_paged_int8(q.data_ptr(), k_codes.data_ptr(), v_codes.data_ptr(),
+                                      float(k_scale), float(v_scale), block_table.data_ptr(),
+                                      seq_lens.data_ptr(), o.data_ptr(),
+                                      lse.data_ptr() if lse is not None else None,
+                                      N, Hq, Hkv, d, page, num_pages, block_table.shape[1],
+                                      float(scale), workspace.data_ptr(), ws_bytes,
+                                      _stream_ptr(q.device, stream))
     _check(st)
 
 

@@ -266,8 +266,12 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
 
 namespace {
 
-// attn_decode_paged and attn_decode_paged_fp8 (fp8: E4M3 pools with scales).
-int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, const void* v_pool,
+// Page formats of the decode entry points (launch_decode_paged's fmt).
+constexpr int kFmtBf16 = 0, kFmtE4m3 = 1, kFmtInt8 = 2;
+
+// attn_decode_paged(_noalloc), attn_decode_paged_fp8 and attn_decode_paged_int8
+// (8-bit code pools with per-tensor scales).
+int decode_common(const char* fn, int fmt, const void* q, const void* k_pool, const void* v_pool,
                   float k_scale, float v_scale, const int32_t* block_table,
                   const int32_t* seq_lens, void* o, float* lse, int N, int Hq, int Hkv, int d,
                   int page, int num_pages, int max_blocks, float scale, int dtype,
@@ -280,7 +284,8 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
     return fail(ATTN_EINVAL, "%s: Hq=%d is not a multiple of Hkv=%d", fn, Hq, Hkv);
   if (!std::isfinite(scale) || !(scale > 0.f))
     return fail(ATTN_EINVAL, "%s: scale must be finite and > 0", fn);
-  if (fp8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
+  const bool codes8 = fmt != kFmtBf16;
+  if (codes8 && (!std::isfinite(k_scale) || !(k_scale > 0.f) || !std::isfinite(v_scale) ||
               !(v_scale > 0.f) || !std::isfinite(scale * k_scale * kLog2e)))
     return fail(ATTN_EINVAL, "%s: k_scale and v_scale must be finite and > 0", fn);
   if (dtype != ATTN_BF16) return fail(ATTN_EUNSUPPORTED, "%s: only bf16 queries are supported", fn);
@@ -313,7 +318,7 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
     if (!aligned(workspace, 16)) return fail(ATTN_EINVAL, "%s: misaligned workspace", fn);
   }
   {
-    const size_t es = fp8 ? 1 : 2;
+    const size_t es = codes8 ? 1 : 2;
     const size_t qb = (size_t)N * Hq * d * 2, pb = (size_t)num_pages * Hkv * kPage * d * es;
     const size_t btb = (size_t)N * max_blocks * 4, nb = (size_t)N * 4;
     const size_t lb = lse ? (size_t)N * Hq * 4 : 0;
@@ -341,9 +346,9 @@ int decode_common(const char* fn, bool fp8, const void* q, const void* k_pool, c
   dw.seg_waves = reinterpret_cast<int2*>(ws);
   dw.o_part = reinterpret_cast<float*>(ws + lay.o_part);
   dw.lse_part = reinterpret_cast<float*>(ws + lay.lse_part);
-  const float scale_log2 = scale * kLog2e * (fp8 ? k_scale : 1.f);
+  const float scale_log2 = scale * kLog2e * (codes8 ? k_scale : 1.f);
   hipError_t e = attn::launch_decode_paged(q, k_pool, v_pool, block_table, seq_lens, o, lse, dw,
-                                           N, Hq, Hkv, d, num_pages, max_blocks, scale_log2, fp8,
+                                           N, Hq, Hkv, d, num_pages, max_blocks, scale_log2, fmt,
                                            v_scale, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(ATTN_EHIP, "%s: %s", fn, hipGetErrorString(e));
   return ATTN_OK;
@@ -358,7 +363,7 @@ int attn_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                       int N, int Hq, int Hkv, int d, int page, int num_pages, int max_blocks,
                       float scale, int dtype, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  return decode_common("attn_decode_paged", false, q, k_pool, v_pool, 1.f, 1.f, block_table,
+  return decode_common("attn_decode_paged", kFmtBf16, q, k_pool, v_pool, 1.f, 1.f, block_table,
                        seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks, scale, dtype,
                        workspace, workspace_bytes, stream);
 }
@@ -367,7 +372,7 @@ int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_p
                               const int32_t* block_table, const int32_t* seq_lens, void* o,
                               float* lse, int N, int Hq, int Hkv, int d, int page, int num_pages,
                               int max_blocks, float scale, int dtype, void* stream) {
-  return decode_common("attn_decode_paged_noalloc", false, q, k_pool, v_pool, 1.f, 1.f,
+  return decode_common("attn_decode_paged_noalloc", kFmtBf16, q, k_pool, v_pool, 1.f, 1.f,
                        block_table, seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks,
                        scale, dtype, nullptr, 0, stream, true);
 }
@@ -377,7 +382,17 @@ int attn_decode_paged_fp8(const void* q, const void* k_pool, const void* v_pool,
                           void* o, float* lse, int N, int Hq, int Hkv, int d, int page,
                           int num_pages, int max_blocks, float scale, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return decode_common("attn_decode_paged_fp8", true, q, k_pool, v_pool, k_scale, v_scale,
+  return decode_common("attn_decode_paged_fp8", kFmtE4m3, q, k_pool, v_pool, k_scale, v_scale,
+                       block_table, seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks,
+                       scale, ATTN_BF16, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_paged_int8(const void* q, const void* k_pool, const void* v_pool, float k_scale,
+                           float v_scale, const int32_t* block_table, const int32_t* seq_lens,
+                           void* o, float* lse, int N, int Hq, int Hkv, int d, int page,
+                           int num_pages, int max_blocks, float scale, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_common("attn_decode_paged_int8", kFmtInt8, q, k_pool, v_pool, k_scale, v_scale,
                        block_table, seq_lens, o, lse, N, Hq, Hkv, d, page, num_pages, max_blocks,
                        scale, ATTN_BF16, workspace, workspace_bytes, stream);
 }

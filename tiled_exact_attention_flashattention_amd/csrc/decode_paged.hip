@@ -105,6 +105,9 @@ template <int D> struct PairRegs<D, true> {
   u32x4 v[VCH];
 };
 
+// Page formats: bf16 values, or 8-bit codes with per-tensor scales.
+constexpr int kFmtBf16 = 0, kFmtE4m3 = 1, kFmtInt8 = 2;
+
 // Eight E4M3 codes (OCP "fn" format, as the conversion unit of this chip
 // reads them) to bf16; every E4M3 value is exact in bf16.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
@@ -113,15 +116,31 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(uint32_t lo, uint32_t hi) {
   return pack_bf16x8(a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]);
 }
 
+// Eight signed (two's-complement) bytes to bf16; every value -128 .. 127 is
+// exact in bf16.
+__device__ __forceinline__ float sbyte(uint32_t w, int i) {
+  return (float)(int)(int8_t)(uint8_t)(w >> (8 * i));
+}
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  return pack_bf16x8(sbyte(lo, 0), sbyte(lo, 1), sbyte(lo, 2), sbyte(lo, 3), sbyte(hi, 0),
+                     sbyte(hi, 1), sbyte(hi, 2), sbyte(hi, 3));
+}
+
+template <int FMT>
+__device__ __forceinline__ bf16x8 codes8_to_bf16(uint32_t lo, uint32_t hi) {
+  if constexpr (FMT == kFmtInt8) return i8x8_to_bf16(lo, hi);
+  else return e4m3x8_to_bf16(lo, hi);
+}
+
 // One page pair, all fields wave-uniform.  n < 0 marks a padding pair.
 struct PairMeta {
   int n, hk, p, np, len, u;   // sequence, KV head, pair in segment, pairs in segment, tokens, unit
   int tv0, tv1;               // tokens of page 0 / page 1 that take part (0: masked)
 };
 
-// FP8: K and V pages hold E4M3 codes; scale_log2 then includes the key
-// scale and v_scale multiplies the output (1 for bf16 pages).
-template <int D, bool FP8>
+// FMT: bf16 pages, or E4M3 / int8 codes; with codes scale_log2 includes the
+// key scale and v_scale multiplies the output (1 for bf16 pages).
+template <int D, int FMT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2)))
 void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ kpool_v,
                           const void* __restrict__ vpool_v, const int32_t* __restrict__ block_table,
@@ -129,6 +148,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ k
                           float* __restrict__ lse, int2* __restrict__ seg_waves,
                           float* __restrict__ o_part, float* __restrict__ lse_part, int N, int Hq,
                           int Hkv, int num_pages, int max_blocks, float scale_log2, float v_scale) {
+  constexpr bool FP8 = FMT != kFmtBf16;       // 8-bit codes (E4M3 or int8)
   using KV = typename std::conditional<FP8, uint8_t, bf16>::type;
   const KV* __restrict__ kpool = static_cast<const KV*>(kpool_v);
   const KV* __restrict__ vpool = static_cast<const KV*>(vpool_v);
@@ -347,7 +367,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ k
           const int slot = ch / (D / 16), col = ch % (D / 16);
           const int row = 16 * p + slot;
           const u32x4 raw = r.v[p * (VCH / 2) + c];
-          const bf16x8 lo = e4m3x8_to_bf16(raw[0], raw[1]), hi = e4m3x8_to_bf16(raw[2], raw[3]);
+          const bf16x8 lo = codes8_to_bf16<FMT>(raw[0], raw[1]), hi = codes8_to_bf16<FMT>(raw[2], raw[3]);
           *reinterpret_cast<u32x4*>(vl + row * D + ((2 * col) ^ dv_swz<D>(row)) * 8) =
               slot < tv ? *reinterpret_cast<const u32x4*>(&lo) : zero;
           *reinterpret_cast<u32x4*>(vl + row * D + ((2 * col + 1) ^ dv_swz<D>(row)) * 8) =
@@ -387,7 +407,7 @@ void decode_stream_kernel(const bf16* __restrict__ q, const void* __restrict__ k
         bf16x8 ka;
         if constexpr (FP8) {
           const u32x4 raw = r.k[p][c >> 1];
-          ka = (c & 1) ? e4m3x8_to_bf16(raw[2], raw[3]) : e4m3x8_to_bf16(raw[0], raw[1]);
+          ka = (c & 1) ? codes8_to_bf16<FMT>(raw[2], raw[3]) : codes8_to_bf16<FMT>(raw[0], raw[1]);
         } else {
           ka = r.k[p][c];
         }
@@ -582,12 +602,12 @@ void decode_combine_kernel(const int32_t* __restrict__ seq_lens, const int2* __r
   if (lse != nullptr && lane == 0) lse[nh] = W > 0.f ? M + logf(W) : -INFINITY;
 }
 
-template <int D, bool FP8>
+template <int D, int FMT>
 hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                     const DecodeWorkspace& ws, int N, int Hq, int Hkv, int num_pages,
                     int max_blocks, float scale_log2, float v_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<D, FP8>), dim3(kDecodeWaves), dim3(64), 0, stream,
+  hipLaunchKernelGGL((decode_stream_kernel<D, FMT>), dim3(kDecodeWaves), dim3(64), 0, stream,
                      static_cast<const bf16*>(q), k_pool, v_pool, block_table, seq_lens,
                      static_cast<bf16*>(o), lse, ws.seg_waves, ws.o_part, ws.lse_part, N, Hq, Hkv,
                      num_pages, max_blocks, scale_log2, v_scale);
@@ -645,18 +665,14 @@ hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_
                                const int32_t* block_table, const int32_t* seq_lens, void* o,
                                float* lse, const DecodeWorkspace& ws, int N, int Hq, int Hkv,
                                int d, int num_pages, int max_blocks, float scale_log2,
-                               bool fp8, float v_scale, hipStream_t stream) {
-  if (fp8)
-    return d == 128 ? launch_d<128, true>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
-                                          Hq, Hkv, num_pages, max_blocks, scale_log2, v_scale,
-                                          stream)
-                    : launch_d<64, true>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
-                                         Hq, Hkv, num_pages, max_blocks, scale_log2, v_scale,
-                                         stream);
-  return d == 128 ? launch_d<128, false>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
-                                         Hq, Hkv, num_pages, max_blocks, scale_log2, 1.f, stream)
-                  : launch_d<64, false>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N,
-                                        Hq, Hkv, num_pages, max_blocks, scale_log2, 1.f, stream);
+                               int fmt, float v_scale, hipStream_t stream) {
+#define ATTN_DECODE_LAUNCH(DD, FF)                                                           \
+  launch_d<DD, FF>(q, k_pool, v_pool, block_table, seq_lens, o, lse, ws, N, Hq, Hkv, num_pages, \
+                   max_blocks, scale_log2, FF == kFmtBf16 ? 1.f : v_scale, stream)
+  if (fmt == kFmtE4m3) return d == 128 ? ATTN_DECODE_LAUNCH(128, kFmtE4m3) : ATTN_DECODE_LAUNCH(64, kFmtE4m3);
+  if (fmt == kFmtInt8) return d == 128 ? ATTN_DECODE_LAUNCH(128, kFmtInt8) : ATTN_DECODE_LAUNCH(64, kFmtInt8);
+  return d == 128 ? ATTN_DECODE_LAUNCH(128, kFmtBf16) : ATTN_DECODE_LAUNCH(64, kFmtBf16);
+#undef ATTN_DECODE_LAUNCH
 }
 
 }  // namespace attn

@@ -68,13 +68,13 @@ static_assert(kDecodeScratchBytes % 256 == 0, "each region of the layout is a mu
 // device current.
 hipError_t decode_scratch(hipStream_t stream, void** ptr);
 
-// fp8: pools hold E4M3 codes; scale_log2 then includes the key scale and
-// v_scale multiplies the output (ignored for bf16 pools).
+// fmt: 0 bf16 pools; 1 E4M3 codes; 2 int8 codes.  With codes scale_log2
+// includes the key scale and v_scale multiplies the output (ignored for bf16).
 hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_pool,
                                const int32_t* block_table, const int32_t* seq_lens,
                                void* o, float* lse, const DecodeWorkspace& ws,
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
-                               float scale_log2, bool fp8, float v_scale, hipStream_t stream);
+                               float scale_log2, int fmt, float v_scale, hipStream_t stream);
 
 // Backward, bf16 in/out, fp32 accumulation on MFMA: the row statistics
 // (LSE * log2 e, D = rowsum(dO * O)) into ws.stats [B*Hq*T][2] floats, then
