@@ -459,9 +459,11 @@ def write_counters(pmc_dir):
     copy_bytes = 256 << 20
     factors = {}
     for counter, sub in (("FETCH_SIZE", "copy_fetch"), ("WRITE_SIZE", "copy_write")):
-        # the copy is the dispatch with the largest reading (KiB per dispatch)
-        kib = max(float(r["Counter_Value"]) for r in rows(sub))
-        factors[counter] = copy_bytes / (kib * 1024.0)
+        # the copy dispatches (the runtime's buffer copy), KiB per dispatch
+        vals = [float(r["Counter_Value"]) for r in rows(sub) if "copy" in r["Kernel_Name"].lower()]
+        if not vals:
+            raise SystemExit(f"no copy dispatch under {pmc_dir}/{sub}")
+        factors[counter] = copy_bytes / (sum(vals) / len(vals) * 1024.0)
 
     out = {"factors": factors, "copy_probe_bytes": copy_bytes,
            "commands": {"copy": "rocprofv3 --pmc <FETCH_SIZE|WRITE_SIZE> --output-format csv -d <dir> "
@@ -517,7 +519,17 @@ def summarize(prof_dir):
     lines = []
 
     def short(name):
-        return name.split("(")[0][:110]
+        import re
+        n = name.replace("(anonymous namespace)::", "")
+        m = re.match(r"_ZN\d+attn\d+_GLOBAL__N_1(\d+)", n)
+        if m:                                  # mangled: identifier and integer template args
+            ln = int(m.group(1))
+            rest = n[m.end():]
+            ident, rest = rest[:ln], rest[ln:]
+            args = re.findall(r"L[a-z](\d+)E", rest.split("EE")[0] + "E") if rest.startswith("I") else []
+            return f"{ident}<{','.join(args)}>" if args else ident
+        m = re.match(r"(?:void\s+)?(?:[\w]+::)*(\w+(?:<.*?>)?)\(", n)
+        return (m.group(1) if m else n)[:90]
 
     for f in traces:
         acc = defaultdict(list)
@@ -594,10 +606,6 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
-    # float32 so that sum() only reads it (an int32 sum would first write an
-    # int64 copy, leaving dirty cache lines whose write-back slows the kernels)
-    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
-
     if args.copy_probe:
         src = torch.ones(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -606,6 +614,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes": 256 << 20, "launches": 5}))
         return
+    # float32 so that sum() only reads it (an int32 sum would first write an
+    # int64 copy, leaving dirty cache lines whose write-back slows the kernels)
+    flush = None if args.no_flush else torch.ones((512 << 20) // 4, dtype=torch.float32, device=dev)
     if args.hbm_probe:
         print(json.dumps(hbm_probe(workloads.decode_5(), dev, stream, flush)), flush=True)
         return
