@@ -13,9 +13,14 @@ launch preceded by a 512 MiB read that evicts L2 and the Infinity Cache:
 `--only <workload>` makes the step that one launch (profiling runs).
 
 Reported (one JSON line on stdout):
-  value               prefill_2 TFLOP/s = algorithmic FLOPs / mean launch time
-                      (HIP events on the launch stream), FLOPs = 4*d per visible
-                      (query, key) pair;
+  value               prefill_2 TFLOP/s = algorithmic FLOPs / mean kernel time,
+                      FLOPs = 4*d per visible (query, key) pair; kernel time
+                      is taken by HIP events that the call's kernels record
+                      themselves as they begin and end (attn_time_next_call),
+                      the interval a kernel trace reports; `ms_stream` beside
+                      each `ms` is the time between events recorded on the
+                      launch stream around the call, which adds the stream's
+                      launch gaps;
   roofline_per_kernel every workload of the step against its published peak
                       (bf16 dense MFMA 2516.6 TFLOP/s; HBM 8 TB/s for decode,
                       bytes = K+V of every cached token once plus q, o, lse,
@@ -45,7 +50,7 @@ Reported (one JSON line on stdout):
   (window, chunked, decode_fp8, decode_int8 and backward each carry their own
   cpu_baseline)
   cpu_baseline        the oracle's figure for the headline workload.
-The flush reads sit outside the kernel events but inside ms_per_step.
+The flush reads sit outside both kinds of events but inside ms_per_step.
 
 Measurement helpers (each runs and exits):
   --copy-probe        a 256 MiB device copy, to calibrate the HBM counters;
@@ -138,21 +143,41 @@ def oracle_sample(budget_s, units, run_unit, work_of):
     return done, work, time.perf_counter() - t0
 
 
-def timed_launches(stream, flush, launch, n=7, skip=2):
-    """Mean HIP-event time (ms) of launch() over n cold launches, the first `skip` untimed."""
+def kernel_events(n):
+    """n pairs of timing events, each recorded once (torch creates an event on
+    its first record), for attn_time_next_call."""
     import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n)]
+    for a, b_ in evs:
+        a.record()
+        b_.record()
+    torch.cuda.synchronize()
+    return evs
+
+
+def timed_launches(stream, flush, launch, n=7, skip=2):
+    """Cold launches of launch(events) (the first `skip` untimed): the mean time
+    from the start of the call's first kernel to the end of its last (events the
+    call's kernels record, passed to launch), and the mean time between stream
+    markers recorded around the call (which adds the stream's launch gaps).
+    Returns (kernel ms, stream ms, launches timed)."""
+    import torch
+    kev = kernel_events(n)
     times = []
     for i in range(n):
         if flush is not None:
             flush.sum()
         a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        launch()
+        launch(kev[i])
         b_.record(stream)
         if i >= skip:
-            times.append((a, b_))
+            times.append((kev[i], (a, b_)))
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b_) for a, b_ in times) / len(times), len(times)
+    km = sum(k0.elapsed_time(k1) for (k0, k1), _ in times) / len(times)
+    sm = sum(a.elapsed_time(b_) for _, (a, b_) in times) / len(times)
+    return km, sm, len(times)
 
 
 def bench_window(tea, workloads, dev, stream, flush, cpu_budget_s=None, window=1024):
@@ -162,12 +187,14 @@ def bench_window(tea, workloads, dev, stream, flush, cpu_budget_s=None, window=1
     xq, xk, xv = (t.to(dev) for t in (x.q, x.k, x.v))
     xo = torch.empty_like(xq)
     xl = torch.empty((x.B, x.Hq, x.T), dtype=torch.float32, device=dev)
-    ms, n = timed_launches(stream, flush, lambda: tea.attn_fwd_window(
-        xq, xk, xv, xo, xl, x.scale, window, stream=stream))
+    ms, ms_stream, n = timed_launches(stream, flush, lambda ev: (
+        tea.attn_time_next_call(*ev),
+        tea.attn_fwd_window(xq, xk, xv, xo, xl, x.scale, window, stream=stream)))
     fl, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, True, 2, window=window)
     tf = fl / (ms * 1e-3) / 1e12
     rec = {"config": f"B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal, "
-                     f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms, "value": tf,
+                     f"window {window}", "kernel": "prefill_bf16_kernel", "ms": ms,
+           "ms_stream": ms_stream, "value": tf,
            "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n,
            "cpu_baseline": None}
@@ -198,13 +225,15 @@ def bench_chunked(tea, workloads, dev, stream, flush, cpu_budget_s=None):
     bt, sl, ql = (torch.from_numpy(a).to(dev) for a in (x.block_table, x.seq_lens, x.q_lens))
     xo = torch.empty_like(xq)
     xl = torch.empty((x.N, x.Hq, x.T), dtype=torch.float32, device=dev)
-    ms, n = timed_launches(stream, flush, lambda: tea.attn_prefill_paged(
-        xq, kp, vp, bt, sl, ql, xo, xl, x.scale, stream=stream))
+    ms, ms_stream, n = timed_launches(stream, flush, lambda ev: (
+        tea.attn_time_next_call(*ev),
+        tea.attn_prefill_paged(xq, kp, vp, bt, sl, ql, xo, xl, x.scale, stream=stream)))
     fl = 4 * x.d * x.Hq * chunked_pairs(x.seq_lens, x.q_lens)
     tf = fl / (ms * 1e-3) / 1e12
     rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, chunk {x.T}, cached "
                      f"{int(x.seq_lens.min())}..{int(x.seq_lens.max())} tokens, d={x.d}, bf16, "
                      f"16-token pages", "kernel": "prefill_bf16_kernel (paged)", "ms": ms,
+           "ms_stream": ms_stream,
            "value": tf, "unit": "TFLOP/s", "algorithmic_flops": fl, "bound": "mfma",
            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS, "launches": n,
            "cpu_baseline": None}
@@ -237,16 +266,19 @@ def bench_decode_q8(tea, workloads, dev, stream, flush, cpu_budget_s=None, fmt="
     xo = torch.empty_like(xq)
     xl = torch.empty((x.N, x.Hq), dtype=torch.float32, device=dev)
     ws = tea.decode_workspace(x.N, x.Hq, x.d, x.max_blocks, dev)
-    ms, n = timed_launches(stream, flush, lambda: entry(
-        xq, kc, vc, x.k_scale, x.v_scale, bt, sl, xo, xl, x.scale, ws, stream=stream), n=12)
+    ms, ms_stream, n = timed_launches(stream, flush, lambda ev: (
+        tea.attn_time_next_call(*ev),
+        entry(xq, kc, vc, x.k_scale, x.v_scale, bt, sl, xo, xl, x.scale, ws, stream=stream)), n=12)
     tokens = int(x.seq_lens.astype("int64").sum())
     pages = int(((x.seq_lens.astype("int64") + x.page - 1) // x.page).sum())
     nbytes = tokens * x.Hkv * x.d * 2 + 2 * x.N * x.Hq * x.d * 2 + x.N * x.Hq * 4 + x.N * 4 + pages * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
     rec = {"config": f"N={x.N}, Hq={x.Hq}, Hkv={x.Hkv}, d={x.d}, "
                      f"{'E4M3' if fmt == 'fp8' else 'int8'} K/V pages, lengths "
-                     f"U[512,8192] (sum {tokens})", "kernel": f"decode_stream_kernel<{fmt}>+"
-                     "decode_combine_kernel", "ms": ms, "value": gbs, "unit": "GB/s",
+                     f"U[512,8192] (sum {tokens})",
+           "kernel": f"decode_stream_kernel<{fmt}>+decode_combine_kernel",
+           "ms": ms, "ms_stream": ms_stream, "value": gbs,
+           "unit": "GB/s",
            "algorithmic_bytes": nbytes, "bound": "hbm", "peak": PEAK_HBM_GBS,
            "frac_of_hbm_peak": gbs / PEAK_HBM_GBS, "launches": n,
            "tokens_per_s": tokens / (ms * 1e-3), "cpu_baseline": None}
@@ -285,26 +317,18 @@ def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
     gq, gk, gv = torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv)
     ws = torch.empty(tea.attn_bwd_workspace_size(x.B, x.Hq, x.Hkv, x.T, x.S, x.d), dtype=torch.uint8,
                      device=dev)
-    times = []
-    for i in range(7):
-        if flush is not None:
-            flush.sum()
-        a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        tea.attn_bwd(xq, xk, xv, xo, xl, xdo, gq, gk, gv, x.scale, x.causal, ws, stream=stream)
-        b_.record(stream)
-        if i >= 2:
-            times.append((a, b_))
-    torch.cuda.synchronize()
-    ms = sum(a.elapsed_time(b_) for a, b_ in times) / len(times)
+    ms, ms_stream, n = timed_launches(stream, flush, lambda ev: (
+        tea.attn_time_next_call(*ev),
+        tea.attn_bwd(xq, xk, xv, xo, xl, xdo, gq, gk, gv, x.scale, x.causal, ws, stream=stream)))
     fwd_flops, _ = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
     flops = fwd_flops // 4 * 10
     tf = flops / (ms * 1e-3) / 1e12
     rec = {"config": f"{x.name}: B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal",
-           "kernels": "bwd_prep_kernel+bwd_dq_kernel+bwd_dkdv_kernel", "ms": ms, "value": tf,
+           "kernels": "bwd_prep_kernel+bwd_dq_kernel+bwd_dkdv_kernel", "ms": ms,
+           "ms_stream": ms_stream, "value": tf,
            "unit": "TFLOP/s", "algorithmic_flops": flops, "bound": "mfma",
            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS,
-           "launches": len(times), "cpu_baseline": None}
+           "launches": n, "cpu_baseline": None}
     del xq, xk, xv, xdo, xo, xl, gq, gk, gv, ws
     if cpu_budget_s:
         import oracle
@@ -403,7 +427,7 @@ def hbm_probe(dinp, dev, stream, flush, launches=12):
                            "`python -m tiled_exact_attention_flashattention_amd.build`")
     L = ctypes.CDLL(B.PROBE_LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int
-    L.attn_probe_read_units.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp]
+    L.attn_probe_read_units.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp]
     L.attn_probe_read_units.restype = i32
     unit_bytes = dinp.page * dinp.d * 2
     units = []
@@ -424,14 +448,17 @@ def hbm_probe(dinp, dev, stream, flush, launches=12):
     res = {}
     for name, (kb, vb, ub) in {"decode_pages": (kp, vpl, u_dev),
                                "sequential": (seq, seq[n * unit_bytes:], seq_units)}.items():
-        def launch():
+        def launch(ev):
             st = L.attn_probe_read_units(kb.data_ptr(), vb.data_ptr(), ub.data_ptr(), n, unit_bytes,
-                                         sink.data_ptr(), waves, ctypes.c_void_p(stream.cuda_stream))
+                                         sink.data_ptr(), waves, ctypes.c_void_p(stream.cuda_stream),
+                                         ctypes.c_void_p(ev[0].cuda_event),
+                                         ctypes.c_void_p(ev[1].cuda_event))
             if st != 0:
                 raise RuntimeError(f"probe launch failed ({st})")
-        ms, cnt = timed_launches(stream, flush, launch, n=launches, skip=2)
+        ms, ms_stream, cnt = timed_launches(stream, flush, launch, n=launches, skip=2)
         nbytes = 2 * n * unit_bytes
-        res[name] = {"bytes": nbytes, "ms": ms, "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
+        res[name] = {"bytes": nbytes, "ms": ms, "ms_stream": ms_stream,
+                     "value": nbytes / (ms * 1e-3) / 1e9, "unit": "GB/s",
                      "frac_of_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
                      "launches": cnt}
     res["note"] = (f"{n} chunks of {unit_bytes} B of K and as many of V ({waves} one-wave "
@@ -644,18 +671,22 @@ def main():
                                                      stream=stream))
 
     events = {name: [] for name in names}
+    kev = {name: kernel_events(args.steps) for name in names}
+    smark = {name: kernel_events(args.steps) for name in names}
 
     def step(record):
         for name in names:
             if flush is not None:
                 flush.sum()
             if record:
-                a, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                i = len(events[name])
+                a, b_ = smark[name][i]
                 a.record(stream)
+                tea.attn_time_next_call(*kev[name][i])
             launchers[name]()
             if record:
                 b_.record(stream)
-                events[name].append((a, b_))
+                events[name].append((kev[name][i], (a, b_)))
 
     for _ in range(args.warmup):
         step(False)
@@ -670,8 +701,9 @@ def main():
     kernels = {}
     for name in names:
         x = inputs[name]
-        times = [a.elapsed_time(b_) for a, b_ in events[name]]
+        times = [k0.elapsed_time(k1) for (k0, k1), _ in events[name]]
         ms = sum(times) / len(times)
+        ms_stream = sum(a.elapsed_time(b_) for _, (a, b_) in events[name]) / len(times)
         if name.startswith("prefill"):
             fl, nb = prefill_work(x.B, x.Hq, x.Hkv, x.T, x.S, x.d, x.causal, 2)
             rate = fl / (ms * 1e-3) / 1e12
@@ -690,6 +722,7 @@ def main():
                    "tokens_per_s": tokens / (ms * 1e-3)}
         rec.update({"traffic": counters_for(name), "algorithmic_flops": fl,
                     "algorithmic_bytes": nb, "ms": ms, "ms_min": min(times),
+                    "ms_stream": ms_stream,
                     "launches": len(times)})
         kernels[name] = rec
 

@@ -42,7 +42,8 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     never allocates, frees, or synchronises, and keeps no state between calls
  *     (except attn_decode_paged_noalloc, whose scratch is a device-resident
- *     array of the library: see there).
+ *     array of the library, and the timing events of attn_time_next_call, which
+ *     last for one call: see there).
  *   - Tensors are dense row-major (C order) with the shapes given below.
  *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
  *     Work is enqueued asynchronously on it; results are valid once the stream
@@ -361,6 +362,24 @@ const char* attn_status_string(int status);
 
 /* Detail of the calling thread's last non-OK return ("" if none yet). */
 const char* attn_last_error(void);
+
+/*
+ * attn_time_next_call -- kernel timing for profiling and benchmarks.
+ *
+ * start_event and stop_event are hipEvent_t handles (created by the caller
+ * with timing enabled), passed as void*.  The calling thread's next call of a
+ * computing entry point (attn_fwd, attn_fwd_window, attn_bwd,
+ * attn_prefill_paged and the attn_decode_paged family) launches its first
+ * kernel so that it records start_event when the kernel begins, and each of
+ * its kernels so that it records stop_event when the kernel ends; after the
+ * call's work has finished, hipEventElapsedTime(start, stop) is the time from
+ * the start of its first kernel to the end of its last, without the time the
+ * stream spends reaching the first kernel.  The events apply to that one call
+ * only, whether it succeeds or fails, and are then forgotten.  Both NULL:
+ * cancels a pending pair.  Exactly one NULL: ATTN_EINVAL.  The events are not
+ * owned by the library.
+ */
+int attn_time_next_call(void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

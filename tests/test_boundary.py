@@ -30,7 +30,8 @@ def test_header_declares_the_expected_entry_points():
                                      "attn_decode_paged_noalloc",
                                      "attn_decode_workspace_size",
                                      "attn_fwd", "attn_fwd_window", "attn_last_error",
-                                     "attn_prefill_paged", "attn_status_string"]
+                                     "attn_prefill_paged", "attn_status_string",
+                                     "attn_time_next_call"]
 
 
 def test_library_loads_and_exports_every_declared_symbol():
@@ -47,6 +48,29 @@ def test_status_strings():
     assert tea.attn_status_string(ATTN_EUNSUPPORTED).startswith("ATTN_EUNSUPPORTED")
     assert tea.attn_status_string(3).startswith("ATTN_EHIP")
     assert "unknown" in tea.attn_status_string(99)
+
+
+def test_time_next_call_takes_both_events_or_neither():
+    L = tea.lib()
+    assert L.attn_time_next_call(None, None) == tea.ATTN_OK
+    assert L.attn_time_next_call(ctypes.c_void_p(16), None) == ATTN_EINVAL
+    assert tea.attn_last_error().startswith("attn_time_next_call")
+    assert L.attn_time_next_call(None, ctypes.c_void_p(16)) == ATTN_EINVAL
+    with pytest.raises(ValueError):
+        class _Uncreated:
+            cuda_event = 0
+        tea.attn_time_next_call(_Uncreated(), _Uncreated())
+
+
+def test_rejected_call_forgets_pending_timing_events():
+    # A pair that is never a real event: if the rejected call kept it, the
+    # next call would hand it to the HIP runtime.  Only host checks run here.
+    L = tea.lib()
+    assert L.attn_time_next_call(ctypes.c_void_p(16), ctypes.c_void_p(32)) == tea.ATTN_OK
+    st = L.attn_fwd(None, None, None, None, None, 1, 1, 1, 1, 1, 64, 1.0, 0, 1, None)
+    assert st == ATTN_EINVAL
+    # cancelling is idempotent and succeeds whether or not a pair is pending
+    assert L.attn_time_next_call(None, None) == tea.ATTN_OK
 
 
 def _r256(x):

@@ -11,7 +11,8 @@ from ._binding import (ATTN_BF16, ATTN_EHIP, ATTN_EINVAL, ATTN_EUNSUPPORTED, ATT
                        attn_decode_paged_noalloc,
                        attn_decode_workspace_size,
                        attn_fwd, attn_fwd_window, attn_last_error, attn_prefill_paged,
-                       attn_status_string, bwd, check_paged_inputs, decode_paged,
+                       attn_status_string, attn_time_next_call, bwd, check_paged_inputs,
+                       decode_paged,
                        decode_workspace, fwd, lib, library_path)
 
 __all__ = [
@@ -19,6 +20,6 @@ __all__ = [
     "AttnError", "attn_bwd", "attn_bwd_workspace_size", "attn_decode_paged", "attn_decode_paged_fp8",
     "attn_decode_paged_int8", "attn_decode_paged_noalloc",
     "attn_decode_workspace_size", "attn_fwd", "attn_fwd_window", "attn_last_error",
-    "attn_prefill_paged", "attn_status_string", "bwd", "check_paged_inputs",
+    "attn_prefill_paged", "attn_status_string", "attn_time_next_call", "bwd", "check_paged_inputs",
     "decode_paged", "decode_workspace", "fwd", "lib", "library_path",
 ]

@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
     L.attn_status_string.restype = ctypes.c_char_p
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
+    L.attn_time_next_call.argtypes = [vp, vp]
+    L.attn_time_next_call.restype = i32
     _LIB = L
     return L
 
@@ -109,6 +111,23 @@ def attn_status_string(status: int) -> str:
 
 def attn_last_error() -> str:
     return lib().attn_last_error().decode()
+
+
+def attn_time_next_call(start, stop) -> None:
+    """The calling thread's next computing call records ``start`` when its
+    first kernel begins and ``stop`` when its last kernel ends.
+
+    start/stop: ``torch.cuda.Event(enable_timing=True)`` objects that have been
+    recorded once (torch creates the underlying event on its first record), or
+    both None to cancel.
+    """
+    if start is None and stop is None:
+        _check(lib().attn_time_next_call(None, None))
+        return
+    handles = [int(e.cuda_event) for e in (start, stop)]
+    if not all(handles):
+        raise ValueError("record each event once before passing it (torch creates it then)")
+    _check(lib().attn_time_next_call(handles[0], handles[1]))
 
 
 def attn_decode_workspace_size(N: int, Hq: int, d: int, max_blocks: int, page: int = PAGE) -> int:

@@ -21,6 +21,13 @@
 namespace {
 
 thread_local char g_last_error[256] = "";
+thread_local attn::CallEvents g_call_events;
+
+// Held by every computing entry point: whatever becomes of the call, timing
+// events set by attn_time_next_call apply to it and to no later call.
+struct CallEventsScope {
+  ~CallEventsScope() { g_call_events = attn::CallEvents{}; }
+};
 
 int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char* fmt, ...) {
@@ -65,7 +72,17 @@ WsLayout decode_workspace_layout(int64_t N, int64_t Hq, int64_t d) {
 
 }  // namespace
 
+attn::CallEvents& attn::call_events() { return g_call_events; }
+
 extern "C" {
+
+int attn_time_next_call(void* start_event, void* stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr))
+    return fail(ATTN_EINVAL, "attn_time_next_call: give both events or neither");
+  g_call_events.start = static_cast<hipEvent_t>(start_event);
+  g_call_events.stop = static_cast<hipEvent_t>(stop_event);
+  return ATTN_OK;
+}
 
 const char* attn_status_string(int status) {
   switch (status) {
@@ -97,6 +114,7 @@ namespace {
 int fwd_common(const char* fn, const void* q, const void* k, const void* v, void* o, float* lse,
                int B, int Hq, int Hkv, int T, int S, int d, float scale, int causal, int window,
                int dtype, void* stream) {
+  CallEventsScope events_scope;
   if (!q || !k || !v || !o) return fail(ATTN_EINVAL, "%s: q, k, v and o must be non-NULL", fn);
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1)
     return fail(ATTN_EINVAL, "%s: sizes must be >= 1 (B=%d Hq=%d Hkv=%d T=%d S=%d d=%d)", fn, B,
@@ -150,7 +168,10 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
 int attn_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int Hq, int Hkv, int T, int S, int d, float scale, int window, int dtype,
                     void* stream) {
-  if (window < 1) return fail(ATTN_EINVAL, "attn_fwd_window: window must be >= 1 (got %d)", window);
+  if (window < 1) {
+    g_call_events = attn::CallEvents{};
+    return fail(ATTN_EINVAL, "attn_fwd_window: window must be >= 1 (got %d)", window);
+  }
   return fwd_common("attn_fwd_window", q, k, v, o, lse, B, Hq, Hkv, T, S, d, scale, 1, window,
                     dtype, stream);
 }
@@ -159,6 +180,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const f
              const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int T, int S,
              int d, float scale, int causal, int dtype, void* workspace, size_t workspace_bytes,
              void* stream) {
+  CallEventsScope events_scope;
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !workspace)
     return fail(ATTN_EINVAL, "attn_bwd: every pointer must be non-NULL");
   if (B < 1 || Hq < 1 || Hkv < 1 || T < 1 || S < 1 || d < 1)
@@ -218,6 +240,7 @@ int attn_prefill_paged(const void* q, const void* k_pool, const void* v_pool,
                        void* o, float* lse, int N, int Hq, int Hkv, int T, int d, int page,
                        int num_pages, int max_blocks, float scale, int window, int dtype,
                        void* stream) {
+  CallEventsScope events_scope;
   const char* fn = "attn_prefill_paged";
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !q_lens || !o)
     return fail(ATTN_EINVAL, "%s: tensor pointers must be non-NULL", fn);
@@ -276,6 +299,7 @@ int decode_common(const char* fn, int fmt, const void* q, const void* k_pool, co
                   const int32_t* seq_lens, void* o, float* lse, int N, int Hq, int Hkv, int d,
                   int page, int num_pages, int max_blocks, float scale, int dtype,
                   void* workspace, size_t workspace_bytes, void* stream, bool noalloc = false) {
+  CallEventsScope events_scope;
   if (!q || !k_pool || !v_pool || !block_table || !seq_lens || !o)
     return fail(ATTN_EINVAL, "%s: tensor pointers must be non-NULL", fn);
   if (N < 1 || Hq < 1 || Hkv < 1 || d < 1 || num_pages < 1 || max_blocks < 1 || page < 1)

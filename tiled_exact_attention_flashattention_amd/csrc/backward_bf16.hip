@@ -622,13 +622,13 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
                         const BwdWorkspace& ws, int B, int Hq, int Hkv, int T, int S, float scale,
                         hipStream_t stream) {
   const long long rows = (long long)B * Hq * T;
-  hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
+  launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
                      static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, ws.stats, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * kLog2e;
   const long long gq = (long long)((T + 127) / 128) * B * Hq;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)gq), dim3(256), 0, stream,
+  launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3((unsigned)gq), dim3(256), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
                      static_cast<bf16*>(dq), B, Hq, Hkv, T, S, scale_log2, scale);
@@ -640,7 +640,7 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
   if (e != hipSuccess) return e;
   const int nsplit = bwd_kv_splits(B, Hq, Hkv, S);
   const long long gkv = (long long)((S + kKvBK - 1) / kKvBK) * B * Hkv * nsplit;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)gkv), dim3(256),
+  launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)gkv), dim3(256),
                      KvStage<D>::kRing, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
@@ -649,7 +649,7 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
   e = hipGetLastError();
   if (e != hipSuccess || nsplit == 1) return e;
   const long long nkv = (long long)B * Hkv * S * D;
-  hipLaunchKernelGGL(bwd_kv_reduce_kernel, dim3((unsigned)((nkv / 4 + 255) / 256)), dim3(256), 0,
+  launch_kernel(bwd_kv_reduce_kernel, dim3((unsigned)((nkv / 4 + 255) / 256)), dim3(256), 0,
                      stream, ws.kv_part, static_cast<bf16*>(dk), static_cast<bf16*>(dv), nkv, nsplit,
                      scale);
   return hipGetLastError();

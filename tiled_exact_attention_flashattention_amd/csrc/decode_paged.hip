@@ -607,13 +607,13 @@ hipError_t launch_d(const void* q, const void* k_pool, const void* v_pool,
                     const int32_t* block_table, const int32_t* seq_lens, void* o, float* lse,
                     const DecodeWorkspace& ws, int N, int Hq, int Hkv, int num_pages,
                     int max_blocks, float scale_log2, float v_scale, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_stream_kernel<D, FMT>), dim3(kDecodeWaves), dim3(64), 0, stream,
+  launch_kernel(decode_stream_kernel<D, FMT>, dim3(kDecodeWaves), dim3(64), 0, stream,
                      static_cast<const bf16*>(q), k_pool, v_pool, block_table, seq_lens,
                      static_cast<bf16*>(o), lse, ws.seg_waves, ws.o_part, ws.lse_part, N, Hq, Hkv,
                      num_pages, max_blocks, scale_log2, v_scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_combine_kernel<D>), dim3(N * Hq), dim3(64), 0, stream, seq_lens,
+  launch_kernel(decode_combine_kernel<D>, dim3(N * Hq), dim3(64), 0, stream, seq_lens,
                      ws.seg_waves, ws.o_part, ws.lse_part, static_cast<bf16*>(o), lse, Hq, Hkv,
                      max_blocks);
   return hipGetLastError();

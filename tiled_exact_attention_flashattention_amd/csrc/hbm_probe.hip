@@ -12,6 +12,7 @@
 // they can arrive with no compute, no block-table walk and no combine.  Given
 // the chunks in ascending order of a contiguous buffer it measures plain
 // sequential reading of the same byte count.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -68,19 +69,30 @@ extern "C" {
 // splitting the units into equal contiguous ranges; writes one word per lane
 // to sink [waves * 64] uint32 (device memory).  unit_bytes must be 1, 2, 4 or
 // 8 KiB; the caller guarantees every addressed unit lies inside its buffers.
+// start_event / stop_event (hipEvent_t, both or neither): recorded as the
+// kernel begins and ends, as the library's attn_time_next_call does.
 // Returns 0, 1 on a bad argument, 3 on a launch error.
 int attn_probe_read_units(const void* k_base, const void* v_base, const int32_t* units,
-                          int n_units, int unit_bytes, uint32_t* sink, int waves, void* stream) {
+                          int n_units, int unit_bytes, uint32_t* sink, int waves, void* stream,
+                          void* start_event, void* stop_event) {
   if (!k_base || !v_base || !units || !sink || n_units < 1 || waves < 1) return 1;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return 1;
   const u32x4* k = static_cast<const u32x4*>(k_base);
   const u32x4* v = static_cast<const u32x4*>(v_base);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  void (*kern)(const u32x4*, const u32x4*, const int32_t*, int, uint32_t*);
   switch (unit_bytes) {
-    case 1024: hipLaunchKernelGGL(probe_read_kernel<1>, dim3(waves), dim3(64), 0, st, k, v, units, n_units, sink); break;
-    case 2048: hipLaunchKernelGGL(probe_read_kernel<2>, dim3(waves), dim3(64), 0, st, k, v, units, n_units, sink); break;
-    case 4096: hipLaunchKernelGGL(probe_read_kernel<4>, dim3(waves), dim3(64), 0, st, k, v, units, n_units, sink); break;
-    case 8192: hipLaunchKernelGGL(probe_read_kernel<8>, dim3(waves), dim3(64), 0, st, k, v, units, n_units, sink); break;
+    case 1024: kern = probe_read_kernel<1>; break;
+    case 2048: kern = probe_read_kernel<2>; break;
+    case 4096: kern = probe_read_kernel<4>; break;
+    case 8192: kern = probe_read_kernel<8>; break;
     default: return 1;
+  }
+  if (e0 == nullptr) {
+    hipLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, k, v, units, n_units, sink);
+  } else {
+    hipExtLaunchKernelGGL(kern, dim3(waves), dim3(64), 0, st, e0, e1, 0u, k, v, units, n_units, sink);
   }
   return hipGetLastError() == hipSuccess ? 0 : 3;
 }

@@ -4,10 +4,34 @@
 // launch status.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace attn {
+
+// Timing events for the calling thread's next library call (attn_time_next_call):
+// its first kernel records `start` as it begins, and each of its kernels records
+// `stop` as it ends, so once the call's work is done `stop` holds the end of its
+// last kernel.  Both null: plain launches.
+struct CallEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+CallEvents& call_events();
+
+// Every kernel of the library is launched through here.
+template <typename K, typename... A>
+inline void launch_kernel(K kernel, dim3 grid, dim3 block, uint32_t lds_bytes, hipStream_t stream,
+                          A... args) {
+  CallEvents& ev = call_events();
+  if (ev.start == nullptr && ev.stop == nullptr) {
+    hipLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, args...);
+  } else {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds_bytes, stream, ev.start, ev.stop, 0u, args...);
+    ev.start = nullptr;
+  }
+}
 
 // Prefill, bf16 in/out, fp32 accumulation on MFMA.  scale_log2 = scale*log2(e).
 // window > 0 (causal only): sliding window of that many keys; 0: none.

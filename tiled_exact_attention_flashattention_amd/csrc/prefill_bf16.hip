@@ -651,7 +651,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
   if (CAUSAL && !PAGED && ((B * Hkv) & 7) == 0 && grid % 256 == 0 &&
       grid <= (long long)per_cu * kXcdCount * kCusPerXcd)
     snake = 1;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, QB, PAGED>), dim3((unsigned)grid),
+  launch_kernel(prefill_bf16_kernel<D, CAUSAL, QB, PAGED>, dim3((unsigned)grid),
                      dim3(kThreads), 0, stream, static_cast<const bf16*>(q),
                      static_cast<const bf16*>(k), static_cast<const bf16*>(v),
                      static_cast<bf16*>(o), lse, B, Hq, Hkv, T, S, scale_log2, window, pkv, snake);

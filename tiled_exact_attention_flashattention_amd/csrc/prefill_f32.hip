@@ -133,7 +133,7 @@ hipError_t launch_one(const void* q, const void* k, const void* v, void* o, floa
                       hipStream_t stream) {
   const long long ntq = (T + kRows - 1) / kRows;
   const long long grid = ntq * B * Hq;
-  hipLaunchKernelGGL((prefill_f32_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kRows), 0, stream,
+  launch_kernel(prefill_f32_kernel<D, CAUSAL>, dim3((unsigned)grid), dim3(kRows), 0, stream,
                      static_cast<const float*>(q), static_cast<const float*>(k),
                      static_cast<const float*>(v), static_cast<float*>(o), lse, B, Hq, Hkv, T, S,
                      scale_log2, window);
