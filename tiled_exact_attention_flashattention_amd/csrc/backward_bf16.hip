@@ -18,16 +18,18 @@
 //     operands, K and V tiles stream through two LDS stages by the
 //     direct-to-LDS load; per tile S^T = K Q^T, dP^T = V dO^T, P, dS, and
 //     dQ^T += K^T dS^T with K^T from the LDS transpose read.
-//   bwd_dkdv_kernel:  one workgroup per 128 keys of one (batch, KV head), one
-//     wave per SIMD; each wave keeps its 32 keys' K and V (two 16-key blocks)
-//     in registers as MFMA B operands and walks every query tile (32 rows) of
-//     every query head of the group (or of its share of them, when the heads
-//     are split between workgroups) that can see them.  Q and dO tiles and their rows' statistics stream through
-//     a four-stage LDS ring by the direct-to-LDS load, so three tiles are in
-//     flight while one is computed (a tile is short: 32 MFMAs per wave).  Per
-//     tile S = Q K^T, dP = dO V^T, P, dS, then dV += P^T dO and dK += dS^T Q
-//     with dO and Q from the transpose read.  Summing the group's heads in
-//     registers keeps the grouped-query reduction exact in order.
+//   bwd_dkdv_kernel:  one workgroup of 8 waves per 128 keys of one (batch, KV
+//     head); a pair of waves shares 32 keys (two 16-key blocks): one keeps
+//     their K as MFMA B operands and accumulates dV, the other keeps V and
+//     accumulates dK.  Both walk every query tile (32 rows) of every query
+//     head of the group (or of its share of them, when the heads are split
+//     between workgroups) that can see the keys.  Q and dO tiles and their
+//     rows' statistics stream through a five-stage LDS ring by the
+//     direct-to-LDS load.  Per tile the dV wave forms S = Q K^T and P, hands
+//     P to its partner through LDS and adds P^T dO; the dK wave, one tile
+//     behind, forms dP = dO V^T and dS = P (dP - D) and adds dS^T Q (dO and Q
+//     from the transpose read).  Summing the group's heads in registers keeps
+//     the grouped-query reduction exact in order.
 // Tiles read both as MFMA row operands and through the transpose read use the
 // dual swizzle of lds_stage.hpp, bank-conflict free for both.
 #include "cdna4.hpp"
@@ -312,31 +314,47 @@ __device__ __forceinline__ void sched_reads_ahead() {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV.  Workgroup = 4 waves x 32 keys (two 16-key blocks per wave), one
-// wave per SIMD: with 32 keys a wave's MFMAs per byte read from LDS double
-// against 16 keys, and the registers that takes (K, V operands and dK, dV
-// accumulators of 32 keys) need the whole register file.  The query heads of
-// a group may be divided between workgroups (head splits) to fill the chip;
-// their fp32 partial dK, dV are then summed in a fixed order by a second kernel.
-constexpr int kKvKeysPerWave = 32;
-constexpr int kKvBK = 4 * kKvKeysPerWave;    // keys per workgroup
+// dK, dV.  Workgroup = 8 waves over 128 keys; wave pair (p, p + 4) shares the
+// 32 keys k0 + 32 p .. + 31 and (waves being dealt to SIMDs in turn) SIMD p.
+//   V side, wave p: the keys' K rows as MFMA B operands and the dV
+//     accumulators; per streamed tile of 32 query rows S = Q K^T, then
+//     P = exp2(scale_log2 S - LSE2) with the mask applied, P (fp32) to LDS for
+//     the partner, dV += P^T dO.
+//   K side, wave p + 4, one tile behind: the keys' V rows and the dK
+//     accumulators; dP = dO V^T, P from LDS, dS = P (dP - D),
+//     dK += dS^T Q.
+// Both sides run the same instruction shape (row-operand MFMAs, an
+// elementwise step, MFMAs on the transpose read), each with half of the
+// operand and accumulator registers a wave needs for both gradients, so two
+// waves fit per SIMD and one side's elementwise work runs beside the other's
+// MFMAs.  The query heads of a group may be divided between workgroups (head
+// splits) to fill the chip; their fp32 partial dK, dV are then summed in a
+// fixed order by a second kernel.
+constexpr int kKvKeysPerPair = 32;
+constexpr int kKvBK = 4 * kKvKeysPerPair;    // keys per workgroup
 constexpr int kKvBQ = 32;                    // query rows per streamed tile
-constexpr int kKvStages = 4;                 // LDS ring depth
+constexpr int kKvStages = 5;                 // ring: the K side's tile, the V side's, 3 in flight
+constexpr int kKvAhead = kKvStages - 2;      // tiles loaded ahead of the V side
 
 // One ring stage: Q tile, dO tile (both [kKvBQ][D] bf16, dual-swizzled
-// chunks) and the tile rows' statistics ([kKvBQ] x (LSE * log2 e, D)).
+// chunks) and the tile rows' statistics ([kKvBQ] x (LSE * log2 e, D)); after
+// the ring, two buffers of P (4 pairs x 16 floats per lane, lane-major).
 template <int D>
 struct KvStage {
   static constexpr int kTile = kKvBQ * D * 2;
   static constexpr int kStats = kKvBQ * 8;
   static constexpr int kBytes = 2 * kTile + kStats;
   static constexpr int kRing = kKvStages * kBytes;
-  static constexpr int kCpw = kKvBQ * (D / 8) / 256;   // 16-byte loads per thread per tile
-  static constexpr int kDmaPerStep = 2 * kCpw + 1;      // per wave: Q, dO, statistics
+  static constexpr int kPBuf = 4 * 64 * 16 * 4;                 // one tile's P of all pairs
+  static constexpr int kLds = kRing + 2 * kPBuf;
+  // 16-byte loads per tile: Q and dO each kKvBQ * D / 8; at D = 128 every
+  // wave loads one of each, at D = 64 waves 0-3 load Q and 4-7 dO
+  static constexpr int kTileLoads = D == 128 ? 2 : 1;
+  static constexpr int kDmaPerStep = kTileLoads + 1;            // + the statistics
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                      const bf16* __restrict__ v, const bf16* __restrict__ dout,
                      const float* __restrict__ stats, bf16* __restrict__ dk,
@@ -347,8 +365,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   constexpr int CPR = D / 8;
   constexpr int NDC = D / 32;
   constexpr int NDB = D / 16;
-  constexpr int CPW = L::kCpw;
-  static_assert(CPW * 256 == BQ * CPR, "tile must split evenly");
+  static_assert(L::kTileLoads * 512 == 2 * BQ * CPR, "tile loads must split evenly");
   extern __shared__ __attribute__((aligned(16))) char ring[];
 
   // ---- (key tile, batch, KV head, head split); head splits vary fastest so
@@ -365,7 +382,10 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, g = lane >> 4;
-  const int kw0 = k0 + kKvKeysPerWave * wave;  // first key of this wave
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+  const bool vside = wave_s < 4;             // V side (dV) or K side (dK)
+  const int pair = wave_s & 3;
+  const int kw0 = k0 + kKvKeysPerPair * pair;   // first key of this pair
   const size_t kvbase = ((size_t)(b * Hkv + hk) * S) * D;
 
   // query tiles that can see some key of this workgroup
@@ -374,29 +394,24 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int nq = max(0, ntq - qt0);
   const int ntiles = nq * hps;               // (head, q tile) pairs, head-major
 
-  // ---- K and V rows of this lane's keys kw0 + 16 kb + l16 as B operands ----
-  bf16x8 kop[2][NDC], vop[2][NDC];
+  // ---- K (V side) or V (K side) rows of this lane's keys kw0 + 16 kb + l16 ----
+  bf16x8 kv[2][NDC];
+  {
+    const bf16* src = vside ? k : v;
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    const size_t roff = kvbase + (size_t)min(kw0 + 16 * kb + l16, S - 1) * D + 8 * g;
+    for (int kb = 0; kb < 2; ++kb) {
+      const size_t roff = kvbase + (size_t)min(kw0 + 16 * kb + l16, S - 1) * D + 8 * g;
 #pragma unroll
-    for (int c = 0; c < NDC; ++c) {
-      kop[kb][c] = *reinterpret_cast<const bf16x8*>(k + roff + 32 * c);
-      vop[kb][c] = *reinterpret_cast<const bf16x8*>(v + roff + 32 * c);
+      for (int c = 0; c < NDC; ++c) kv[kb][c] = *reinterpret_cast<const bf16x8*>(src + roff + 32 * c);
     }
   }
 
   // ---- direct-to-LDS loads of one ring stage ----
-  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-  uint32_t toff[CPW];
-  int lrow[CPW];
-#pragma unroll
-  for (int r = 0; r < CPW; ++r) {
-    const int p = 64 * (wave * CPW + r) + lane;
-    const int row = p / CPR, cph = p % CPR;
-    lrow[r] = row;
-    toff[r] = (uint32_t)(row * D + (cph ^ dual_swz<D>(row)) * 8) * 2u;
-  }
+  // chunk p of the wave's share: row p / CPR, 16-byte chunk p % CPR of Q (and
+  // of dO at D = 128; at D = 64 the K side's waves take dO)
+  const int lp = 64 * (D == 128 ? wave : (wave & 3)) + lane;
+  const int lrow = lp / CPR;
+  const uint32_t toff = (uint32_t)(lrow * D + ((lp % CPR) ^ dual_swz<D>(lrow)) * 8) * 2u;
   const uint32_t ring_lds = lds_addr(ring);
   auto head_of = [&](int t) { return h_first + t / nq; };
   auto row0_of = [&](int t) { return (qt0 + t % nq) * BQ; };
@@ -410,29 +425,28 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const bf16* qg = q + hbase * D;
     const bf16* og = dout + hbase * D;
     const uint32_t sb = ring_lds + (uint32_t)((t % kKvStages) * L::kBytes);
-    const uint32_t ql = sb + (uint32_t)(wave_s * CPW) * 1024u;
-    const uint32_t ol = ql + (uint32_t)L::kTile;
-    const bool full = row0 + BQ <= T;
-#pragma unroll
-    for (int r = 0; r < CPW; ++r) {
-      const int rr = full ? row0 + lrow[r] : min(row0 + lrow[r], T - 1);   // rows past T re-read T-1
-      const uint32_t add = (uint32_t)((rr - lrow[r]) * D) * 2u;
-      lds_dma16(qg, toff[r] + add, ql + 1024u * r);
-      lds_dma16(og, toff[r] + add, ol + 1024u * r);
+    const int rr = row0 + lrow < T ? row0 + lrow : T - 1;      // rows past T re-read T-1
+    const uint32_t off = toff + (uint32_t)((rr - lrow) * D) * 2u;
+    const uint32_t dst = (uint32_t)(64 * 16 * (D == 128 ? wave_s : (wave_s & 3)));
+    if (D == 128) {
+      lds_dma16(qg, off, sb + dst);
+      lds_dma16(og, off, sb + (uint32_t)L::kTile + dst);
+    } else {
+      lds_dma16(vside ? qg : og, off, sb + (vside ? 0u : (uint32_t)L::kTile) + dst);
     }
-    // statistics of rows row0 + 8 wave .. + 7: 16 dwords from this wave
-    if (lane < 16) {
-      const int row = min(row0 + 8 * wave + (lane >> 1), T - 1);
+    // statistics of rows row0 + 4 wave .. + 3: 8 dwords from this wave
+    if (lane < 8) {
+      const int row = min(row0 + 4 * wave + (lane >> 1), T - 1);
       lds_dma4(stats + 2 * hbase, (uint32_t)(row * 8 + (lane & 1) * 4),
-               sb + (uint32_t)(2 * L::kTile + 64 * wave_s));
+               sb + (uint32_t)(2 * L::kTile + 32 * wave_s));
     }
   };
 
-  f32x4 dka[2][NDB], dva[2][NDB];            // dK[key][d], dV[key][d] per 16-key block
+  f32x4 acc[2][NDB];                         // dV (V side) or dK (K side) [key][d] per 16-key block
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) dka[kb][db] = dva[kb][db] = f32x4{};
+    for (int db = 0; db < NDB; ++db) acc[kb][db] = f32x4{};
 
   const int t_row = 4 * g + (l16 >> 2);
   const int t_chunk = (l16 & 3) >> 1;
@@ -440,144 +454,155 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   const int sw_lo = dual_swz<D>(t_row), sw_hi = dual_swz<D>(t_row + 16);
   const int swz_l = dual_swz<D>(l16);
   const bool edge_keys = k0 + kKvBK > S;     // some key of the workgroup is past S
+  f32x4* pbuf = reinterpret_cast<f32x4*>(ring + L::kRing);   // [2][4 pairs][4][64 lanes]
 
+  // Tile t on this side: the V side's tile of step t, the K side's of step t + 1.
   auto compute_tile = [&](int t) {
     const char* sp = ring + (t % kKvStages) * L::kBytes;
     const bf16* qs = reinterpret_cast<const bf16*>(sp);
     const bf16* os = reinterpret_cast<const bf16*>(sp + L::kTile);
     const float4* st = reinterpret_cast<const float4*>(sp + 2 * L::kTile);
+    const bf16* xs = vside ? qs : os;        // row operands of the first product
+    const bf16* ys = vside ? os : qs;        // transpose-read operands of the second
+    f32x4* pslot = pbuf + ((size_t)((t & 1) * 4 + pair) * 4) * 64 + lane;
     const int row0 = row0_of(t);
-    // S[row][key] = Q K^T and dP[row][key] = dO V^T (rows 16 qb + 4 g + i, column key)
-    f32x4 s[2][2], dp[2][2];
+    // r[row][key] = X kv^T: S = Q K^T (V side) or dP = dO V^T (K side),
+    // rows 16 qb + 4 g + i, column key 16 kb + l16
+    f32x4 r[2][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) s[qb][0] = s[qb][1] = dp[qb][0] = dp[qb][1] = f32x4{};
-    // all operand reads first: one wave per SIMD hides LDS latency only by
-    // having many reads in flight
-    bf16x8 qa[NDC][2], oa[NDC][2];
+    for (int qb = 0; qb < 2; ++qb) r[qb][0] = r[qb][1] = f32x4{};
+    bf16x8 xa[NDC][2];
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const int off = (16 * qb + l16) * D + (((4 * c + g) ^ swz_l) * 8);
-        qa[c][qb] = *reinterpret_cast<const bf16x8*>(qs + off);
-        oa[c][qb] = *reinterpret_cast<const bf16x8*>(os + off);
-      }
+      for (int qb = 0; qb < 2; ++qb)
+        xa[c][qb] = *reinterpret_cast<const bf16x8*>(xs + (16 * qb + l16) * D + (((4 * c + g) ^ swz_l) * 8));
 #pragma unroll
     for (int c = 0; c < NDC; ++c)
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          s[qb][kb] = mfma_16x16x32(qa[c][qb], kop[kb][c], s[qb][kb]);
-          dp[qb][kb] = mfma_16x16x32(oa[c][qb], vop[kb][c], dp[qb][kb]);
-        }
+        for (int kb = 0; kb < 2; ++kb) r[qb][kb] = mfma_16x16x32(xa[c][qb], kv[kb][c], r[qb][kb]);
     // keep the reads of two d-chunks ahead of the MFMAs that use them
-    sched_reads_ahead<NDC, 4, 8>();
-    // P = exp2(scale_log2 s - LSE2) and dS = P (dP - D), zero off the visible pairs
-    float pv[2][2][4], dsw[2][2][4];         // [kb][qb][i]
+    sched_reads_ahead<NDC, 2, 4>();
+    // A operands of the second product: row = this lane's key, k-slots = rows
+    // 4g..4g+3 then 16+4g..16+4g+3
+    bf16x8 op[2];
+    if (vside) {
+      // P = exp2(scale_log2 s - LSE2), zero off the visible pairs
+      float pv[2][2][4];                     // [kb][qb][i]
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      // (LSE * log2 e, D) of rows 16 qb + 4 g + 0..3
-      const float4 ab = st[8 * qb + 2 * g], cd = st[8 * qb + 2 * g + 1];
-      const float lse2[4] = {ab.x, ab.z, cd.x, cd.z};
-      const float dd[4] = {ab.y, ab.w, cd.y, cd.w};
+      for (int qb = 0; qb < 2; ++qb) {
+        const float4 ab = st[8 * qb + 2 * g], cd = st[8 * qb + 2 * g + 1];
+        const float lse2[4] = {ab.x, ab.z, cd.x, cd.z};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pv[kb][qb][i] = exp2_hw(__builtin_fmaf(r[qb][kb][i], scale_log2, -lse2[i]));
+      }
+      if (edge_keys || row0 + BQ > T || (CAUSAL && k0 + kKvBK - 1 > row0 + (S - T))) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int key = kw0 + 16 * kb + l16;
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = row0 + 16 * qb + 4 * g + i;
+              const bool hide = key >= S || row >= T || (CAUSAL && key > row + (S - T));
+              pv[kb][qb][i] = hide ? 0.f : pv[kb][qb][i];
+            }
+        }
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[kb][qb][i] = exp2_hw(__builtin_fmaf(s[qb][kb][i], scale_log2, -lse2[i]));
-          dsw[kb][qb][i] = dp[qb][kb][i] - dd[i];
-        }
-    }
-    if (edge_keys || row0 + BQ > T || (CAUSAL && k0 + kKvBK - 1 > row0 + (S - T))) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = kw0 + 16 * kb + l16;
-#pragma unroll
         for (int qb = 0; qb < 2; ++qb)
+          pslot[(2 * kb + qb) * 64] = f32x4{pv[kb][qb][0], pv[kb][qb][1], pv[kb][qb][2], pv[kb][qb][3]};
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = row0 + 16 * qb + 4 * g + i;
-            const bool hide = key >= S || row >= T || (CAUSAL && key > row + (S - T));
-            pv[kb][qb][i] = hide ? 0.f : pv[kb][qb][i];
-          }
+      for (int kb = 0; kb < 2; ++kb)
+        op[kb] = pack_bf16x8(pv[kb][0][0], pv[kb][0][1], pv[kb][0][2], pv[kb][0][3],
+                             pv[kb][1][0], pv[kb][1][1], pv[kb][1][2], pv[kb][1][3]);
+    } else {
+      // dS = P (dP - D), P as the partner wrote it (masked)
+      float dsv[2][2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float4 ab = st[8 * qb + 2 * g], cd = st[8 * qb + 2 * g + 1];
+        const float dd[4] = {ab.y, ab.w, cd.y, cd.w};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const f32x4 p4 = pslot[(2 * kb + qb) * 64];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dsv[kb][qb][i] = p4[i] * (r[qb][kb][i] - dd[i]);
+        }
       }
-    }
-    // A operands: row = this lane's key, k-slots = rows 4g..4g+3 then 16+4g..16+4g+3
-    bf16x8 pta[2], dsta[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      pta[kb] = pack_bf16x8(pv[kb][0][0], pv[kb][0][1], pv[kb][0][2], pv[kb][0][3],
-                            pv[kb][1][0], pv[kb][1][1], pv[kb][1][2], pv[kb][1][3]);
-      dsta[kb] = pack_bf16x8(pv[kb][0][0] * dsw[kb][0][0], pv[kb][0][1] * dsw[kb][0][1],
-                             pv[kb][0][2] * dsw[kb][0][2], pv[kb][0][3] * dsw[kb][0][3],
-                             pv[kb][1][0] * dsw[kb][1][0], pv[kb][1][1] * dsw[kb][1][1],
-                             pv[kb][1][2] * dsw[kb][1][2], pv[kb][1][3] * dsw[kb][1][3]);
+      for (int kb = 0; kb < 2; ++kb)
+        op[kb] = pack_bf16x8(dsv[kb][0][0], dsv[kb][0][1], dsv[kb][0][2], dsv[kb][0][3],
+                             dsv[kb][1][0], dsv[kb][1][1], dsv[kb][1][2], dsv[kb][1][3]);
     }
-    // dV += P^T dO and dK += dS^T Q, the B operands from the transpose read
-    bf16x8 ob[NDB], qbo[NDB];
+    // acc += op Y: dV += P^T dO (V side) or dK += dS^T Q (K side), Y from the
+    // transpose read
+    bf16x8 yb[NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       const int ch = 2 * db + t_chunk;
       const int off_lo = t_row * D + t_in + (ch ^ sw_lo) * 8;
       const int off_hi = (t_row + 16) * D + t_in + (ch ^ sw_hi) * 8;
-      ob[db] = concat_tr(lds_read_tr16(os + off_lo), lds_read_tr16(os + off_hi));
-      qbo[db] = concat_tr(lds_read_tr16(qs + off_lo), lds_read_tr16(qs + off_hi));
+      yb[db] = concat_tr(lds_read_tr16(ys + off_lo), lds_read_tr16(ys + off_hi));
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        dva[kb][db] = mfma_16x16x32(pta[kb], ob[db], dva[kb][db]);
-        dka[kb][db] = mfma_16x16x32(dsta[kb], qbo[db], dka[kb][db]);
-      }
-    sched_reads_ahead<NDB, 4, 4>();
+      for (int kb = 0; kb < 2; ++kb) acc[kb][db] = mfma_16x16x32(op[kb], yb[db], acc[kb][db]);
+    sched_reads_ahead<NDB, 2, 2>();
   };
 
   if (ntiles > 0) {
 #pragma unroll
-    for (int t = 0; t < kKvStages - 1; ++t) issue(t);
+    for (int t = 0; t < kKvAhead; ++t) issue(t);
     // K and V register loads settle here, not at a first use inside the loop
     // (see the dQ kernel)
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(kop[kb][c]), "v"(vop[kb][c]));
-    for (int t = 0; t < ntiles; ++t) {
-      // this wave's loads of tile t are done once at most the two later
-      // tiles' loads are outstanding; the barrier then publishes every wave's
-      // part and frees the stage of tile t - 1 for tile t + 3
-      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits((kKvStages - 2) * L::kDmaPerStep));
+      for (int c = 0; c < NDC; ++c) asm volatile("" ::"v"(kv[kb][c]));
+    // Step t: the V side computes tile t, the K side tile t - 1 (with the P
+    // its partner wrote in step t - 1).  This wave's loads of tile t are done
+    // once at most the two later tiles' loads are outstanding; the barrier
+    // then publishes every wave's part of tile t and the P of tile t - 1, and
+    // frees the stage of tile t - 2 for tile t + 3.
+    for (int t = 0; t <= ntiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits((kKvAhead - 1) * L::kDmaPerStep));
       stage_barrier();
-      issue(t + kKvStages - 1);
-      compute_tile(t);
+      issue(t + kKvAhead);
+      if (vside ? t < ntiles : t >= 1) compute_tile(vside ? t : t - 1);
     }
     // the re-loads past the last tile land before the workgroup's LDS is released
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0 | vmcnt_bits(0));
   }
 
-  // ---- rows key 16 kb + 4 g + i of the wave's 32, columns 16 db + l16 ----
+  // ---- rows key 16 kb + 4 g + i of the pair's 32, columns 16 db + l16 ----
+  const float osc = vside ? 1.f : scale;     // dK = scale dS^T Q
   if (nsplit == 1) {
+    bf16* dst = vside ? dv : dk;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int kr = kw0 + 16 * kb + 4 * g + i;
         if (kr < S) {
-          bf16* kp = dk + kvbase + (size_t)kr * D + l16;
-          bf16* vp = dv + kvbase + (size_t)kr * D + l16;
+          bf16* rp = dst + kvbase + (size_t)kr * D + l16;
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            kp[16 * db] = (bf16)(dka[kb][db][i] * scale);
-            vp[16 * db] = (bf16)dva[kb][db][i];
-          }
+          for (int db = 0; db < NDB; ++db) rp[16 * db] = (bf16)(acc[kb][db][i] * osc);
         }
       }
   } else {
     // fp32 partials of this head split: part[split][0: dK, 1: dV][B*Hkv*S*D]
     const size_t nkv = (size_t)B * Hkv * S * D;
-    float* pk = part + (size_t)(2 * split) * nkv + kvbase;
-    float* pvv = pk + nkv;
+    float* pp = part + (size_t)(2 * split + (vside ? 1 : 0)) * nkv + kvbase;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -585,10 +610,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         const int kr = kw0 + 16 * kb + 4 * g + i;
         if (kr < S) {
 #pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            pk[(size_t)kr * D + 16 * db + l16] = dka[kb][db][i];
-            pvv[(size_t)kr * D + 16 * db + l16] = dva[kb][db][i];
-          }
+          for (int db = 0; db < NDB; ++db) pp[(size_t)kr * D + 16 * db + l16] = acc[kb][db][i];
         }
       }
   }
@@ -636,12 +658,12 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
   if (e != hipSuccess) return e;
   // the ring is above the 64 KB of static LDS at d = 128
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),
-                          hipFuncAttributeMaxDynamicSharedMemorySize, KvStage<D>::kRing);
+                          hipFuncAttributeMaxDynamicSharedMemorySize, KvStage<D>::kLds);
   if (e != hipSuccess) return e;
   const int nsplit = bwd_kv_splits(B, Hq, Hkv, S);
   const long long gkv = (long long)((S + kKvBK - 1) / kKvBK) * B * Hkv * nsplit;
-  launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)gkv), dim3(256),
-                     KvStage<D>::kRing, stream,
+  launch_kernel(bwd_dkdv_kernel<D, CAUSAL>, dim3((unsigned)gkv), dim3(512),
+                     KvStage<D>::kLds, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
                      static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
                      static_cast<bf16*>(dk), static_cast<bf16*>(dv), ws.kv_part, B, Hq, Hkv, T, S,
