@@ -371,17 +371,23 @@ void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       }
       return;
     }
+    if (full) {
+      // the tile's offset goes into the scalar base: no per-lane arithmetic
+      const bf16* kt = kg + (size_t)j * BN * D;
+      const bf16* vt = vg + (size_t)j * BN * D;
 #pragma unroll
-    for (int r = 0; r < CPW; ++r) {
-      uint32_t add;
-      if (full) {
-        add = (uint32_t)(j * BN * D) * 2u;
-      } else {
-        const int key = min(j * BN + lrow[r], S - 1);
-        add = (uint32_t)((key - lrow[r]) * D) * 2u;
+      for (int r = 0; r < CPW; ++r) {
+        lds_dma16(kt, koff[r], kl + 1024u * r);
+        lds_dma16(vt, voff[r], vl + 1024u * r);
       }
-      lds_dma16(kg, koff[r] + add, kl + 1024u * r);
-      lds_dma16(vg, voff[r] + add, vl + 1024u * r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < CPW; ++r) {
+        const int key = min(j * BN + lrow[r], S - 1);
+        const uint32_t add = (uint32_t)((key - lrow[r]) * D) * 2u;
+        lds_dma16(kg, koff[r] + add, kl + 1024u * r);
+        lds_dma16(vg, voff[r] + add, vl + 1024u * r);
+      }
     }
   };
 
