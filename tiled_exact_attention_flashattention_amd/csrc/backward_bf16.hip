@@ -140,17 +140,23 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const uint32_t kl = lds_addr(ks) + (uint32_t)(wave_s * CPW) * 1024u;
     const uint32_t vl = lds_addr(vs) + (uint32_t)(wave_s * CPW) * 1024u;
     const bool full = (j + 1) * BN <= S;
+    if (full) {
+      // the tile's offset goes into the scalar base: no per-lane arithmetic
+      const void* kt = uniform_ptr(kg + (size_t)j * BN * D);
+      const void* vt = uniform_ptr(vg + (size_t)j * BN * D);
 #pragma unroll
-    for (int r = 0; r < CPW; ++r) {
-      uint32_t add;
-      if (full) {
-        add = (uint32_t)(j * BN * D) * 2u;
-      } else {
-        const int key = min(j * BN + lrow[r], S - 1);
-        add = (uint32_t)((key - lrow[r]) * D) * 2u;
+      for (int r = 0; r < CPW; ++r) {
+        lds_dma16(kt, toff[r], kl + 1024u * r);
+        lds_dma16(vt, toff[r], vl + 1024u * r);
       }
-      lds_dma16(kg, toff[r] + add, kl + 1024u * r);
-      lds_dma16(vg, toff[r] + add, vl + 1024u * r);
+    } else {
+#pragma unroll
+      for (int r = 0; r < CPW; ++r) {
+        const int key = min(j * BN + lrow[r], S - 1);
+        const uint32_t add = (uint32_t)((key - lrow[r]) * D) * 2u;
+        lds_dma16(kg, toff[r] + add, kl + 1024u * r);
+        lds_dma16(vg, toff[r] + add, vl + 1024u * r);
+      }
     }
   };
 
@@ -422,11 +428,13 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     const int tc = min(t, ntiles - 1);
     const int h = head_of(tc), row0 = row0_of(tc);
     const size_t hbase = (size_t)(b * Hq + h) * T;
-    const bf16* qg = q + hbase * D;
-    const bf16* og = dout + hbase * D;
     const uint32_t sb = ring_lds + (uint32_t)((t % kKvStages) * L::kBytes);
-    const int rr = row0 + lrow < T ? row0 + lrow : T - 1;      // rows past T re-read T-1
-    const uint32_t off = toff + (uint32_t)((rr - lrow) * D) * 2u;
+    // a full tile's first row goes into the scalar base; rows past T re-read T-1
+    const bool full = row0 + BQ <= T;
+    const size_t rbase = hbase + (full ? (size_t)row0 : 0);
+    const void* qg = uniform_ptr(q + rbase * D);
+    const void* og = uniform_ptr(dout + rbase * D);
+    const uint32_t off = full ? toff : toff + (uint32_t)(((row0 + lrow < T ? row0 + lrow : T - 1) - lrow) * D) * 2u;
     const uint32_t dst = (uint32_t)(64 * 16 * (D == 128 ? wave_s : (wave_s & 3)));
     if (D == 128) {
       lds_dma16(qg, off, sb + dst);
@@ -437,7 +445,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     // statistics of rows row0 + 4 wave .. + 3: 8 dwords from this wave
     if (lane < 8) {
       const int row = min(row0 + 4 * wave + (lane >> 1), T - 1);
-      lds_dma4(stats + 2 * hbase, (uint32_t)(row * 8 + (lane & 1) * 4),
+      lds_dma4(uniform_ptr(stats + 2 * hbase), (uint32_t)(row * 8 + (lane & 1) * 4),
                sb + (uint32_t)(2 * L::kTile + 32 * wave_s));
     }
   };
