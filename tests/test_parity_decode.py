@@ -145,21 +145,27 @@ def test_decode_rejects_small_workspace():
 
 # Work-distribution cases: the page pairs of all sequences are divided evenly
 # over up to 1024 waves, so these exercise several 64-sequence planning
-# chunks, runs of empty sequences, totals too small for every wave (down to a
-# single wave), and one sequence cut into many pieces (more than 16, the
-# combine's load batch, and more than 64, its lane count).
+# chunks (up to 4000 sequences), runs of empty sequences, totals too small
+# for every wave (down to a single wave), and one sequence cut into many
+# pieces (more than 16, the combine's load batch, and more than 64, its lane
+# count).
 # name, N, Hq, Hkv, d, lens (0: the sequence is emptied on the device)
 def _dist_cases():
     rng = np.random.default_rng(31)
     many = rng.integers(0, 301, 150)
     many[::7] = 0
     mid = rng.integers(1, 4000, 60)
+    lots = rng.integers(0, 49, 4000)
+    lots[::9] = 0
     return [
         ("many_seqs_chunks", 150, 8, 2, 128, many.tolist()),
         ("tiny_total_one_wave", 3, 12, 2, 128, [1, 0, 2]),
         ("zeros_at_ends", 70, 4, 1, 64, [0] * 5 + mid.tolist() + [0] * 5),
         ("one_long_sequence", 1, 12, 2, 128, [8192]),
         ("one_very_long_sequence", 1, 8, 1, 128, [65536]),
+        # every wave plans over 63 chunks of 64 lengths; most sequences are
+        # cut between waves or lie inside one, a ninth are empty
+        ("four_thousand_short_sequences", 4000, 4, 1, 64, lots.tolist()),
     ]
 
 
