@@ -305,9 +305,9 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 
 // Instruction order for a run of N steps that each take R LDS reads and M
 // MFMAs: the reads of the first two steps, then per step its M MFMAs followed
-// by the reads of the step two ahead.  With one wave per SIMD the only cover
-// for LDS latency is reads in flight; left alone the scheduler pulls each
-// read next to its first use.
+// by the reads of the step two ahead.  With few waves per SIMD the main
+// cover for LDS latency is reads in flight; left alone the scheduler pulls
+// each read next to its first use.
 template <int N, int R, int M>
 __device__ __forceinline__ void sched_reads_ahead() {
   constexpr int kDsRead = 0x100, kMfma = 0x008;
