@@ -324,7 +324,7 @@ def bench_backward(tea, workloads, dev, stream, flush, cpu_budget_s):
     flops = fwd_flops // 4 * 10
     tf = flops / (ms * 1e-3) / 1e12
     rec = {"config": f"{x.name}: B={x.B}, Hq={x.Hq}, Hkv={x.Hkv}, T=S={x.T}, d={x.d}, bf16, causal",
-           "kernels": "bwd_prep_kernel+bwd_dq_kernel+bwd_dkdv_kernel", "ms": ms,
+           "kernels": "bwd_dq_kernel+bwd_dkdv_kernel+bwd_kv_reduce_kernel", "ms": ms,
            "ms_stream": ms_stream, "value": tf,
            "unit": "TFLOP/s", "algorithmic_flops": flops, "bound": "mfma",
            "peak": PEAK_BF16_TFLOPS, "frac_of_mfma_peak": tf / PEAK_BF16_TFLOPS,

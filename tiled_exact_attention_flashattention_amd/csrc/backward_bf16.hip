@@ -10,14 +10,15 @@
 // the chain rule of the forward definition (the same scores, causal mask and
 // grouped-query mapping as attn_fwd).
 //
-// Three kernels, no atomics, so results are bit-reproducible:
-//   bwd_prep_kernel:  per query row the pair (LSE * log2 e, D = rowsum(dO * O))
-//     in fp32, into the workspace: the row statistics both other kernels read.
+// Two kernels (three with head splits), no atomics, so results are
+// bit-reproducible:
 //   bwd_dq_kernel:    one workgroup per 128 query rows of one (batch, head),
 //     shaped like the forward kernel: Q and dO stay in registers as MFMA B
 //     operands, K and V tiles stream through two LDS stages by the
 //     direct-to-LDS load; per tile S^T = K Q^T, dP^T = V dO^T, P, dS, and
-//     dQ^T += K^T dS^T with K^T from the LDS transpose read.
+//     dQ^T += K^T dS^T with K^T from the LDS transpose read.  Its prologue
+//     forms each row's statistics (LSE * log2 e, D = rowsum(dO * O)) in fp32
+//     and writes them to the workspace for the dK/dV kernel.
 //   bwd_dkdv_kernel:  one workgroup of 8 waves per 128 keys of one (batch, KV
 //     head); a pair of waves shares 32 keys (two 16-key blocks): one keeps
 //     their K as MFMA B operands and accumulates dV, the other keeps V and
@@ -40,27 +41,6 @@ namespace attn {
 namespace {
 
 // ---------------------------------------------------------------------------
-// Row statistics (LSE * log2 e, D = rowsum(dO * O)): 16 lanes per row, D/16
-// elements per lane.  stats holds two floats per query row.
-template <int D>
-__global__ __launch_bounds__(256)
-void bwd_prep_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
-                     const float* __restrict__ lse, float* __restrict__ stats, long long rows) {
-  constexpr int PER = D / 16;
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int j = threadIdx.x & 15;
-  if (row >= rows) return;                   // whole 16-lane groups leave together
-  const bf16* op = o + row * D + j * PER;
-  const bf16* dp = dout + row * D + j * PER;
-  float acc = 0.f;
-#pragma unroll
-  for (int e = 0; e < PER; ++e) acc = __builtin_fmaf((float)op[e], (float)dp[e], acc);
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-  if (j == 0) *reinterpret_cast<float2*>(stats + 2 * row) = make_float2(lse[row] * kLog2e, acc);
-}
-
-// ---------------------------------------------------------------------------
 // dQ.  Workgroup = 4 waves x 32 query rows (two 16-row blocks per wave).
 constexpr int kDqBN = 64;                    // keys per K/V tile
 
@@ -68,7 +48,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                    const bf16* __restrict__ v, const bf16* __restrict__ dout,
-                   const float* __restrict__ stats, bf16* __restrict__ dq, int B, int Hq,
+                   const bf16* __restrict__ o, const float* __restrict__ lse,
+                   float* __restrict__ stats, bf16* __restrict__ dq, int B, int Hq,
                    int Hkv, int T, int S,
                    float scale_log2, float scale) {
   constexpr int BN = kDqBN;
@@ -167,23 +148,31 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int row = wrow0 + 16 * qb + l16;
+    float dpart = 0.f;                       // this lane's share of rowsum(dO * O)
     if (row < T) {
       const bf16* qp = q + qbase + (size_t)row * D + 8 * g;
       const bf16* dp = dout + qbase + (size_t)row * D + 8 * g;
+      const bf16* op = o + qbase + (size_t)row * D + 8 * g;
 #pragma unroll
       for (int c = 0; c < NDC; ++c) {
         qop[qb][c] = *reinterpret_cast<const bf16x8*>(qp + 32 * c);
         dop[qb][c] = *reinterpret_cast<const bf16x8*>(dp + 32 * c);
+        const bf16x8 ov = *reinterpret_cast<const bf16x8*>(op + 32 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) dpart = __builtin_fmaf((float)dop[qb][c][e], (float)ov[e], dpart);
       }
-      const float2 st = *reinterpret_cast<const float2*>(stats + 2 * ((size_t)(b * Hq + h) * T + row));
-      lse2[qb] = st.x;
-      dd[qb] = st.y;
+      lse2[qb] = lse[(size_t)(b * Hq + h) * T + row] * kLog2e;
     } else {
 #pragma unroll
       for (int c = 0; c < NDC; ++c) qop[qb][c] = dop[qb][c] = bf16x8{};
       lse2[qb] = 0.f;
-      dd[qb] = 0.f;
     }
+    // the four lanes of a row (g = 0..3) hold its D / 4 chunks of 8 elements each
+    dpart += __shfl_xor(dpart, 16);
+    dpart += __shfl_xor(dpart, 32);
+    dd[qb] = dpart;
+    if (row < T && g == 0)
+      *reinterpret_cast<float2*>(stats + 2 * ((size_t)(b * Hq + h) * T + row)) = make_float2(lse2[qb], dpart);
     row_lim[qb] = CAUSAL ? min(row + (S - T), S - 1) : S - 1;
   }
 
@@ -651,18 +640,14 @@ hipError_t launch_bwd_d(const void* q, const void* k, const void* v, const void*
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,
                         const BwdWorkspace& ws, int B, int Hq, int Hkv, int T, int S, float scale,
                         hipStream_t stream) {
-  const long long rows = (long long)B * Hq * T;
-  launch_kernel(bwd_prep_kernel<D>, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream,
-                     static_cast<const bf16*>(o), static_cast<const bf16*>(dout), lse, ws.stats, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const float scale_log2 = scale * kLog2e;
   const long long gq = (long long)((T + 127) / 128) * B * Hq;
   launch_kernel(bwd_dq_kernel<D, CAUSAL>, dim3((unsigned)gq), dim3(256), 0, stream,
                      static_cast<const bf16*>(q), static_cast<const bf16*>(k),
-                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout), ws.stats,
+                     static_cast<const bf16*>(v), static_cast<const bf16*>(dout),
+                     static_cast<const bf16*>(o), lse, ws.stats,
                      static_cast<bf16*>(dq), B, Hq, Hkv, T, S, scale_log2, scale);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // the ring is above the 64 KB of static LDS at d = 128
   e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, CAUSAL>),

@@ -100,9 +100,9 @@ hipError_t launch_decode_paged(const void* q, const void* k_pool, const void* v_
                                int N, int Hq, int Hkv, int d, int num_pages, int max_blocks,
                                float scale_log2, int fmt, float v_scale, hipStream_t stream);
 
-// Backward, bf16 in/out, fp32 accumulation on MFMA: the row statistics
-// (LSE * log2 e, D = rowsum(dO * O)) into ws.stats [B*Hq*T][2] floats, then
-// dQ, then dK and dV; when the query heads of a group are divided between
+// Backward, bf16 in/out, fp32 accumulation on MFMA: dQ, whose kernel also
+// writes the row statistics (LSE * log2 e, D = rowsum(dO * O)) into ws.stats
+// [B*Hq*T][2] floats, then dK and dV; when the query heads of a group are divided between
 // workgroups (bwd_kv_splits > 1), their fp32 partials go to ws.kv_part
 // [splits][2][B*Hkv*S*d] and a last kernel sums them.  No atomics.
 constexpr int kBwdTargetBlocks = 512;   // dK/dV workgroups wanted: two rounds of 256 CUs
