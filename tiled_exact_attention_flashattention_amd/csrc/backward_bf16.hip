@@ -292,22 +292,6 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
   }
 }
 
-// Instruction order for a run of N steps that each take R LDS reads and M
-// MFMAs: the reads of the first two steps, then per step its M MFMAs followed
-// by the reads of the step two ahead.  With few waves per SIMD the main
-// cover for LDS latency is reads in flight; left alone the scheduler pulls
-// each read next to its first use.
-template <int N, int R, int M>
-__device__ __forceinline__ void sched_reads_ahead() {
-  constexpr int kDsRead = 0x100, kMfma = 0x008;
-  __builtin_amdgcn_sched_group_barrier(kDsRead, R * (N < 2 ? N : 2), 0);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
-    if (i + 2 < N) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // dK, dV.  Workgroup = 8 waves over 128 keys; wave pair (p, p + 4) shares the
 // 32 keys k0 + 32 p .. + 31 and (waves being dealt to SIMDs in turn) SIMD p.
@@ -480,8 +464,8 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) r[qb][kb] = mfma_16x16x32(xa[c][qb], kv[kb][c], r[qb][kb]);
-    // keep the reads of two d-chunks ahead of the MFMAs that use them
-    sched_reads_ahead<NDC, 2, 4>();
+    // keep the reads of three d-chunks ahead of the MFMAs that use them
+    sched_reads_ahead<NDC, 2, 4, 3>();
     // A operands of the second product: row = this lane's key, k-slots = rows
     // 4g..4g+3 then 16+4g..16+4g+3
     bf16x8 op[2];
@@ -554,7 +538,7 @@ void bwd_dkdv_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) acc[kb][db] = mfma_16x16x32(op[kb], yb[db], acc[kb][db]);
-    sched_reads_ahead<NDB, 2, 2>();
+    sched_reads_ahead<NDB, 2, 2, 3>();
   };
 
   if (ntiles > 0) {

@@ -133,6 +133,22 @@ __device__ __forceinline__ float fmax2(float a, float b) { return __builtin_fmax
 __device__ __forceinline__ u32x4 load16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void store16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Instruction order for a run of N steps that each take R LDS reads and M
+// MFMAs: the reads of the first A steps, then per step its M MFMAs followed
+// by the reads of the step A ahead.  With few waves per SIMD the main cover
+// for LDS latency is reads in flight; left alone the scheduler pulls each
+// read next to its first use.  Place it in the block that holds the run.
+template <int N, int R, int M, int A>
+__device__ __forceinline__ void sched_reads_ahead() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, R * (N < A ? N : A), 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, M, 0);
+    if (i + A < N) __builtin_amdgcn_sched_group_barrier(kDsRead, R, 0);
+  }
+}
+
 // Workgroup-id remap that keeps the workgroups of one logical group on one
 // XCD.  The dispatcher hands workgroup ids to the 8 XCDs round-robin, so id
 // `pid` runs on XCD pid % 8 as that XCD's (pid / 8)-th workgroup.  Returns the
