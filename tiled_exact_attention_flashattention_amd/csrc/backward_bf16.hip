@@ -209,6 +209,10 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
           dp[1][kk] = mfma_16x16x32(vop, dop[1][dc], dp[1][kk]);
         }
       }
+      // at d = 128 the K and V reads go four units ahead of their MFMAs, and
+      // below the transpose reads four ahead of theirs (backward_3 856 -> 830
+      // us, bit-identical; at d = 64 1-2 % slower, so left to the scheduler)
+      if constexpr (D == 128) sched_reads_ahead<NDC * 2, 2, 4, 4>();
       // dS^T = P^T * (dP^T - D), P^T = exp2(scale_log2 s - LSE2), then zero
       // on keys a row cannot see (only tiles that need it: a select folded
       // into the loop above would cost two VALU instructions per score on
@@ -249,6 +253,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
         dqt[0][db] = mfma_16x16x32(ktop, dsop[0], dqt[0][db]);
         dqt[1][db] = mfma_16x16x32(ktop, dsop[1], dqt[1][db]);
       }
+      if constexpr (D == 128) sched_reads_ahead<NDB, 2, 2, 4>();
     }
   };
 
