@@ -66,6 +66,27 @@ def test_timed_decode_spans_both_kernels():
     assert 0.0 < kms <= sms
 
 
+def test_timed_backward_spans_its_three_kernels():
+    # one KV head of four query heads at S = 256: the dK/dV pass splits the
+    # query heads, so the call runs the dQ, dK/dV and reduction kernels
+    inp = workloads.make_prefill(1, 4, 1, 256, 256, 128, causal=True, seed=45)
+    announce("attn_bwd timed: B=1 Hq=4 Hkv=1 T=S=256 d=128 causal (three kernels)")
+    q, k, v = inp.q.cuda(), inp.k.cuda(), inp.v.cuda()
+    o, lse = tea.fwd(q, k, v, scale=inp.scale, causal=True)
+    do = torch.randn(q.shape, generator=torch.Generator().manual_seed(46)).to(q.dtype).cuda()
+    ws = torch.empty(tea.attn_bwd_workspace_size(1, 4, 1, 256, 256, 128), dtype=torch.uint8,
+                     device="cuda")
+    g1 = tea.bwd(q, k, v, o, lse, do, scale=inp.scale, causal=True, workspace=ws)
+    torch.cuda.synchronize()
+    out = {}
+    kms, sms = _timed(lambda: out.update(g=tea.bwd(q, k, v, o, lse, do, scale=inp.scale,
+                                                   causal=True, workspace=ws)))
+    for a, b in zip(g1, out["g"]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    print(f"kernels {kms * 1e3:.1f} us, stream markers {sms * 1e3:.1f} us")
+    assert 0.0 < kms <= sms
+
+
 def test_events_apply_to_one_call_only():
     inp = workloads.make_prefill(1, 2, 2, 256, 256, 64, causal=False, seed=47)
     announce("attn_fwd events then an untimed call: B=1 H=2 T=S=256 d=64")
