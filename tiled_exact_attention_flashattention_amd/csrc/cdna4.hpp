@@ -49,8 +49,9 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b,
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Hardware base-2 exponential (v_exp_f32).  exp2(-inf) == 0.  Used on
-// arguments <= 0 only, so results lie in [0, 1].
+// Hardware base-2 exponential (v_exp_f32).  exp2(-inf) == 0.  Its arguments
+// are at most 0 (decode, fp32 prefill, backward) or at most the bf16
+// prefill's lazy slack of 8, so results lie in [0, 1] or [0, 2^8].
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Transposed 4 x 16-bit read from LDS (see the header comment).

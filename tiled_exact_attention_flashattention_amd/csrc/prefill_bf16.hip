@@ -10,12 +10,15 @@
 // fusion accelerate AI models", section on FlashAttention-style attention).
 // exp2 replaces exp with log2(e) folded into the scale ("Accelerating Mamba-2
 // with high-performance forward-pass kernels in NVIDIA CUDA Tile", first
-// kernel); since m is the running maximum every exponent is <= 0.
+// kernel).  The reference maximum is lazy: it moves only when a tile's
+// maximum passes it by more than kLazyTau, so every exponent is at most
+// kLazyTau (2^8 stays far inside bf16 and fp32 range).
 //
 // gfx950 mapping:
 //   * one workgroup = 4 waves = 128 query rows of one (batch, query head);
 //     each wave owns 32 rows as two 16-row blocks and keeps their Q in
-//     registers as MFMA B-operands for the whole kernel;
+//     registers as MFMA B-operands for the whole kernel (grids too small to
+//     fill the chip take one 16-row block per wave, 64 rows a workgroup);
 //   * K and V tiles of BN keys go HBM -> LDS by the gfx950 direct-to-LDS load
 //     (no register staging), into two stages held in separate LDS objects:
 //     the load of tile j+1 runs while tile j is computed, one barrier per
@@ -24,7 +27,8 @@
 //     4 keys of one query row per 16-key block, and the exponentiated scores
 //     of two adjacent blocks are exactly the P operand of one P.V MFMA; V^T
 //     comes from the row-major V tile through the LDS transpose read; every K
-//     and V operand read from LDS feeds the MFMAs of both row blocks;
+//     and V operand read from LDS feeds the MFMAs of both row blocks, and the
+//     K reads run four operands ahead of their MFMAs;
 //   * K and V tiles are stored unpadded with their 16-byte chunks XOR-swizzled
 //     per row so that both operand read patterns are bank-conflict free;
 //   * causal: K/V tiles past the workgroup's last visible key are never
