@@ -108,3 +108,76 @@ def test_backward_sweep(case):
     rq, rk, rv = oracle.attention_backward(qd, kd, vd, dod, inp.scale, causal)
     for got, ref, what in ((dq, rq, "dq"), (dk, rk, "dk"), (dv, rv, "dv")):
         check_grad(to_np(got), ref, f"{name} {what}")
+
+
+def _draw_decode(n, seed):
+    """n decode shapes (N, Hq, Hkv, d, min_len, max_len)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 4, 6, 8, 16]))
+        d = int(rng.choice([64, 128]))
+        nseq = int(rng.choice([int(rng.integers(1, 8)), int(rng.integers(8, 200))]))
+        lo = int(rng.integers(1, 600))
+        hi = lo + int(rng.integers(0, 4000))
+        out.append((nseq, hkv * grp, hkv, d, lo, hi))
+    return out
+
+
+DEC = _draw_decode(12, SWEEP_SEED + 2)
+
+
+@pytest.mark.parametrize("case", DEC, ids=[f"N{c[0]}_Hq{c[1]}_Hkv{c[2]}_d{c[3]}_len{c[4]}-{c[5]}"
+                                           for c in DEC])
+def test_decode_sweep(case):
+    nseq, hq, hkv, d, lo, hi = case
+    name = f"decode N{nseq} Hq{hq} Hkv{hkv} d{d} len {lo}-{hi}"
+    inp = workloads.make_decode(nseq, hq, hkv, d, lo, hi, seed=seed_of(name), poison_tail=True,
+                                name=name)
+    announce(f"sweep attn_decode_paged {name}")
+    q, kp, vp = inp.q.cuda(), inp.k_pool.cuda(), inp.v_pool.cuda()
+    bt, sl = torch.from_numpy(inp.block_table).cuda(), torch.from_numpy(inp.seq_lens).cuda()
+    o, lse = tea.decode_paged(q, kp, vp, bt, sl, scale=inp.scale)
+    torch.cuda.synchronize()
+    qd, kd, vd = inp.f64()
+    o_ref, lse_ref = oracle.decode_paged(qd, kd, vd, inp.block_table, inp.seq_lens, inp.scale,
+                                         page=inp.page)
+    check_o(to_np(o), o_ref, "bf16", name)
+    check_lse(to_np(lse), lse_ref, name)
+
+
+def _draw_chunked(n, seed):
+    """n chunked-prefill shapes (N, Hq, Hkv, T, d, min_len, max_len, window)."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        hkv = int(rng.choice([1, 2, 4]))
+        grp = int(rng.choice([1, 2, 3, 6]))
+        d = int(rng.choice([64, 128]))
+        nseq = int(rng.integers(1, 10))
+        t = int(rng.integers(1, 400))
+        lo = int(rng.integers(1, 500))
+        hi = lo + int(rng.integers(0, 1500))
+        window = int(rng.integers(1, 600)) if rng.random() < 0.3 else 0
+        out.append((nseq, hkv * grp, hkv, t, d, lo, hi, window))
+    return out
+
+
+CHUNKED = _draw_chunked(10, SWEEP_SEED + 3)
+
+
+@pytest.mark.parametrize("case", CHUNKED, ids=[
+    f"N{c[0]}_Hq{c[1]}_Hkv{c[2]}_T{c[3]}_d{c[4]}_len{c[5]}-{c[6]}" + (f"_w{c[7]}" if c[7] else "")
+    for c in CHUNKED])
+def test_chunked_prefill_sweep(case):
+    from tests.test_parity_prefill_paged import _check, _run
+    nseq, hq, hkv, t, d, lo, hi, window = case
+    name = f"chunked N{nseq} Hq{hq} Hkv{hkv} T{t} d{d} len {lo}-{hi} w{window}"
+    inp = workloads.make_prefill_paged(nseq, hq, hkv, t, d, lo, hi, window=window,
+                                       seed=seed_of(name), poison_tail=True, extra_pages=3,
+                                       name=name)
+    announce(f"sweep attn_prefill_paged {name}: seq_lens={inp.seq_lens.tolist()} "
+             f"q_lens={inp.q_lens.tolist()}")
+    o, lse = _run(inp)
+    _check(inp, name, o, lse)
