@@ -536,8 +536,9 @@ def counters_for(name):
 
 def summarize(prof_dir):
     """Markdown summary of a rocprofv3 run under prof_dir: per (kernel, grid)
-    dispatch count and mean / min / max duration from the kernel trace, or the
-    mean of every counter per (kernel, grid) from a counter collection."""
+    dispatch count and mean / median / min / max duration from the kernel
+    trace, or the mean of every counter per (kernel, grid) from a counter
+    collection."""
     import csv
     import glob
     from collections import defaultdict
@@ -565,11 +566,13 @@ def summarize(prof_dir):
             acc[(r["Kernel_Name"], grid)].append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
         lines += [f"kernel trace `{os.path.relpath(f, prof_dir)}`", "",
-                  "| kernel | grid (threads) | dispatches | mean µs | min µs | max µs |",
-                  "|---|---|---|---|---|---|"]
+                  "| kernel | grid (threads) | dispatches | mean µs | median µs | min µs | max µs |",
+                  "|---|---|---|---|---|---|---|"]
         for (k, g), d in sorted(acc.items(), key=lambda kv: -sum(kv[1])):
-            lines.append(f"| `{short(k)}` | {g} | {len(d)} | {sum(d) / len(d):.2f} | {min(d):.2f} | "
-                         f"{max(d):.2f} |")
+            ds = sorted(d)
+            med = ds[len(ds) // 2] if len(ds) % 2 else (ds[len(ds) // 2 - 1] + ds[len(ds) // 2]) / 2
+            lines.append(f"| `{short(k)}` | {g} | {len(d)} | {sum(d) / len(d):.2f} | {med:.2f} | "
+                         f"{min(d):.2f} | {max(d):.2f} |")
         lines.append("")
     for f in counters:
         acc = defaultdict(lambda: defaultdict(list))
