@@ -25,7 +25,7 @@
 //     accumulates dK.  Both walk every query tile (32 rows) of every query
 //     head of the group (or of its share of them, when the heads are split
 //     between workgroups) that can see the keys.  Q and dO tiles and their
-//     rows' statistics stream through a five-stage LDS ring by the
+//     rows' statistics stream through a four-stage LDS ring by the
 //     direct-to-LDS load.  Per tile the dV wave forms S = Q K^T and P, hands
 //     P to its partner through LDS and adds P^T dO; the dK wave, one tile
 //     behind, forms dP = dO V^T and dS = P (dP - D) and adds dS^T Q (dO and Q
@@ -317,7 +317,7 @@ void bwd_dq_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
 constexpr int kKvKeysPerPair = 32;
 constexpr int kKvBK = 4 * kKvKeysPerPair;    // keys per workgroup
 constexpr int kKvBQ = 32;                    // query rows per streamed tile
-constexpr int kKvStages = 5;                 // ring: the K side's tile, the V side's, 3 in flight
+constexpr int kKvStages = 4;                 // ring: the K side's tile, the V side's, 2 in flight
 constexpr int kKvAhead = kKvStages - 2;      // tiles loaded ahead of the V side
 
 // One ring stage: Q tile, dO tile (both [kKvBQ][D] bf16, dual-swizzled
