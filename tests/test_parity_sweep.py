@@ -181,3 +181,22 @@ def test_chunked_prefill_sweep(case):
              f"q_lens={inp.q_lens.tolist()}")
     o, lse = _run(inp)
     _check(inp, name, o, lse)
+
+
+# The quantised page formats over the same kind of draw (fewer shapes).
+QDEC = _draw_decode(6, SWEEP_SEED + 4)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("case", QDEC, ids=[f"N{c[0]}_Hq{c[1]}_Hkv{c[2]}_d{c[3]}_len{c[4]}-{c[5]}"
+                                            for c in QDEC])
+def test_quantised_decode_sweep(case, fmt):
+    nseq, hq, hkv, d, lo, hi = case
+    name = f"decode {fmt} N{nseq} Hq{hq} Hkv{hkv} d{d} len {lo}-{hi}"
+    make = workloads.make_decode_fp8 if fmt == "fp8" else workloads.make_decode_int8
+    inp = make(nseq, hq, hkv, d, lo, hi, seed=seed_of(name), poison_tail=True, name=name)
+    if fmt == "fp8":
+        from tests.test_parity_decode_fp8 import _check
+    else:
+        from tests.test_parity_decode_int8 import _check
+    _check(inp, name)
