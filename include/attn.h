@@ -352,8 +352,8 @@ int attn_decode_paged_noalloc(const void* q, const void* k_pool, const void* v_p
 
 /* Bytes of workspace attn_decode_paged needs for these sizes (0 if invalid):
  * r(N * Hq * 8) (which workers hold each sequence's pieces)
- * + r(2 * 1024 * 16 * d * 4) (partial outputs) + r(2 * 1024 * 16 * 4) (their
- * log-sum-exps), r() rounding up to a multiple of 256; about 17 MB at
+ * + r(2 * 768 * 16 * d * 4) (partial outputs) + r(2 * 768 * 16 * 4) (their
+ * log-sum-exps), r() rounding up to a multiple of 256; about 13 MB at
  * d = 128.  It does not depend on max_blocks. */
 size_t attn_decode_workspace_size(int N, int Hq, int d, int max_blocks, int page);
 

@@ -79,13 +79,13 @@ def _r256(x):
 
 def _decode_ws(N, Hq, d):
     """Layout documented in include/attn.h: segment waves, partials, their LSEs."""
-    waves, gmax = 1024, 16
+    waves, gmax = 768, 16
     return _r256(N * Hq * 8) + _r256(2 * waves * gmax * d * 4) + _r256(2 * waves * gmax * 4)
 
 
 def test_workspace_size_formula():
     assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == _decode_ws(64, 12, 128)
-    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == 16914432
+    assert tea.attn_decode_workspace_size(64, 12, 128, 512, 16) == 12687360
     assert tea.attn_decode_workspace_size(1, 1, 64, 1, 16) == _decode_ws(1, 1, 64)
     # independent of max_blocks (the split is decided on the device)
     assert tea.attn_decode_workspace_size(8, 4, 64, 7, 16) == tea.attn_decode_workspace_size(8, 4, 64, 9000, 16)

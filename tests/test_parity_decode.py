@@ -144,7 +144,7 @@ def test_decode_rejects_small_workspace():
 
 
 # Work-distribution cases: the page pairs of all sequences are divided evenly
-# over up to 1024 waves, so these exercise several 64-sequence planning
+# over up to 768 waves, so these exercise several 64-sequence planning
 # chunks (up to 4000 sequences), runs of empty sequences, totals too small
 # for every wave (down to a single wave), and one sequence cut into many
 # pieces (more than 16, the combine's load batch, and more than 64, its lane

@@ -64,12 +64,13 @@ hipError_t launch_prefill_f32(const void* q, const void* k, const void* v, void*
 // Paged decode: a persistent grid of kDecodeWaves single-wave workgroups that
 // split all page pairs evenly, then a combine kernel for the sequences they
 // cut.  Workspace pieces, all 16-byte aligned, laid out by the C ABI layer:
-// Four waves per CU: enough 16 KiB page pairs in flight to keep HBM busy,
-// and half the pieces per sequence (partials to merge) of eight per CU.
+// Three waves per CU: enough 16 KiB page pairs in flight to keep HBM busy
+// with fewer pieces per sequence (partials to merge) than four or more; a
+// whole number per CU so that no CU holds more waves than the others.
 #ifndef DECODE_WAVES
-#define DECODE_WAVES 1024
+#define DECODE_WAVES 768
 #endif
-constexpr int kDecodeWaves = DECODE_WAVES;   // 4 per CU on 256 CUs
+constexpr int kDecodeWaves = DECODE_WAVES;   // 3 per CU on 256 CUs
 constexpr int kDecodeMaxG = 16;      // query heads per KV head, slot stride
 
 struct DecodeWorkspace {
