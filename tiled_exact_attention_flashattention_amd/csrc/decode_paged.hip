@@ -14,7 +14,7 @@
 // Work distribution.  The unit of work is a page pair (32 keys) of one
 // (sequence, KV head) segment; units are numbered sequence-major, then KV
 // head, then pair.  A persistent grid of kDecodeWaves single-wave workgroups
-// (4 per CU on 256 CUs) splits the U units into equal contiguous ranges, so
+// (3 per CU on 256 CUs) splits the U units into equal contiguous ranges, so
 // every CU carries the same load: the kernel is bound by HBM and a CU's share
 // of the bandwidth grows with the waves it holds, so an uneven spread of
 // waves over CUs, not the bytes in flight, is what a fixed split size loses.
